@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Block-sparse causal prefill benchmark on one MI355X.
+
+One step = one layer's whole hot path through the C ABI:
+fp_block_pool (pool Q/K, V^T layout) -> fp_block_select (scores, max
+threshold, lists) -> fp_sparse_prefill (attention over the kept blocks), on
+seeded synthetic inputs already resident in HBM.  The default workload is the
+Llama-3-8B-shaped layer at L = 131072 (32 q / 8 kv heads, d = 128, B = 128,
+bf16, tau = 0.1).
+
+Prints ONE JSON line: value = kept-block TFLOP/s over the whole step
+(algorithmic FLOPs of the kept (query, key) pairs / ms per layer), plus
+per-stage times, the attention kernel's roofline and the CPU oracle timed on
+a bounded sample of the same layer on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill ms/layer + kept-block TFLOP/s (frac of MFMA peak) at 128K"
+# MI355X published peaks
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3, "hbm_gbs": 8000.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4",
+                    help="workload key: c1 c2 c3 c4 c4_fp8 c4_dense c5")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kept_pairs(counts, L, B):
+    """Causal (query, key) pairs of the kept blocks: off-diagonal blocks are
+    full (j < i), the diagonal contributes n_i(n_i+1)/2."""
+    import numpy as np
+    nb = counts.shape[1]
+    n = np.full(nb, B, dtype=np.float64)
+    n[-1] = L - (nb - 1) * B
+    c = counts.astype(np.float64)
+    return float((n[None, :] * B * (c - 1.0) + n[None, :] * (n[None, :] + 1) / 2.0).sum())
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+ATTN_SOURCES = ["block_sparse_long_04_amd/csrc/attn_mfma.hip",
+                "block_sparse_long_04_amd/csrc/common.h"]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, only if it was taken on the current attention source."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != source_hash(ATTN_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(layer_dev, lists_gpu, counts, cfg, tau, budget_s):
+    """The CPU oracle (as it stands) on a bounded sample of the same layer:
+    pool all blocks of the sampled kv heads' keys, then select + attend sampled
+    (head, query-block) rows, heaviest first, until the time budget is spent.
+    Also compares those rows with the GPU (selection outside the tie zone,
+    output error on the GPU's mask)."""
+    import numpy as np
+    import torch
+
+    import oracle.flashprefill_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    L, B, d = cfg.seq_len, cfg.block_size, cfg.head_dim
+    G = cfg.group
+    nb = cfg.num_blocks
+    sc = 1.0 / math.sqrt(d)
+    heads = [0, cfg.num_q_heads // 2 + 1] if cfg.num_q_heads > 1 else [0]
+    kvh = sorted({h // G for h in heads})
+    lay = layer_dev
+
+    def host(t, g, scale):
+        x = t[:, g:g + 1, :].float()
+        if t.dtype == torch.float8_e4m3fn:
+            x = x * scale
+        return x.cpu().numpy()
+
+    kh = {g: host(lay.k, g, lay.k_scale) for g in kvh}
+    vh = {g: host(lay.v, g, lay.v_scale) for g in kvh}
+    rng = np.random.default_rng(0)
+    per_head = []
+    for h in heads:
+        order = list(np.argsort(-counts[h], kind="stable")[:4]) + list(rng.permutation(nb))
+        seen, lst = set(), []
+        for i in order:
+            if int(i) not in seen:
+                seen.add(int(i))
+                lst.append((h, int(i)))
+        per_head.append(lst)
+    rows = [r for tup in zip(*per_head) for r in tup]  # heads interleaved
+    qfull = np.zeros((L, 1, d), np.float32)  # rows s:e are filled per sampled block
+    t0 = time.perf_counter()
+    kbar = {g: O.pool(kh[g], B)[0] for g in kvh}
+    t_pool_k = time.perf_counter() - t0
+    done, flops, tsel, tatt, tq = [], 0.0, 0.0, 0.0, 0.0
+    sel_bad, max_abs, sum_abs, n_abs = 0, 0.0, 0.0, 0
+    kbar_all = None
+    start = time.perf_counter()
+    for (h, i) in rows:
+        if time.perf_counter() - start > budget_s and len(done) >= 4:
+            break
+        g = h // G
+        s, e = i * B, min((i + 1) * B, L)
+        ta = time.perf_counter()
+        qrows = lay.q[s:e, h:h + 1, :].float()
+        if lay.q.dtype == torch.float8_e4m3fn:
+            qrows = qrows * lay.q_scale
+        qrows = qrows.cpu().numpy()
+        tq += time.perf_counter() - ta
+        ta = time.perf_counter()
+        qbar = O.pool(qrows, B)[0, 0]
+        if kbar_all is None:
+            kbar_all = np.zeros((cfg.num_kv_heads, nb, d), np.float32)
+            for gg in kvh:
+                kbar_all[gg] = kbar[gg]
+        kept, m, srow, amb = O.select_rows(qbar[None], kbar_all, [(h, i)], tau, sc, G)[0]
+        tb = time.perf_counter()
+        tsel += tb - ta
+        # attention of the sampled row (oracle mask), float64
+        qfull[s:e] = qrows
+        out = O.attend_row_block(qfull, kh[g], vh[g], 0, i, kept, B, sc, 1)
+        tatt += time.perf_counter() - tb
+        n_i = e - s
+        flops += 4.0 * d * (n_i * B * (len(kept) - 1) + n_i * (n_i + 1) / 2.0)
+        done.append((h, i))
+        # parity of this row against the GPU
+        gl = np.zeros(i + 1, bool)
+        gl[lists_gpu(h, i)] = True
+        ol = np.zeros(i + 1, bool)
+        ol[kept] = True
+        sel_bad += int(((gl != ol) & ~amb).sum())
+        gout = lay.out[s:e, h, :].float().cpu().numpy()
+        want = O.attend_row_block(qfull, kh[g], vh[g], 0, i, lists_gpu(h, i), B, sc, 1)
+        err = np.abs(gout - want)
+        max_abs = max(max_abs, float(err.max()))
+        sum_abs += float(err.sum())
+        n_abs += err.size
+    total = t_pool_k + tsel + tatt
+    return {
+        "value": flops / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(done)} (head, query-block) rows of heads {heads} (4 heaviest + random), "
+                   f"keys of kv heads {kvh} pooled in full; float64 attention, fp32 selection; "
+                   f"{total:.1f} s of CPU work"),
+        "seconds": {"pool_k": round(t_pool_k, 3), "select": round(tsel, 3),
+                    "attention": round(tatt, 3)},
+        "parity_rows": {"rows": len(done), "selection_mismatch_outside_tie_zone": sel_bad,
+                        "out_max_abs": max_abs, "out_mean_abs": sum_abs / max(n_abs, 1)},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures the single-GPU path; this build has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from block_sparse_long_04_amd import _lib
+    from block_sparse_long_04_amd.inputs import CONFIGS, make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.load_library()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.config]
+    tau = cfg.taus[0] if args.tau is None else args.tau
+    print(f"[bench] building {cfg.name} on the GPU", file=sys.stderr, flush=True)
+    layer = make_layer(cfg, device=dev, keep_fp32=False)
+    pf = _lib.Prefill(layer.q, layer.k, layer.v, block_size=cfg.block_size, threshold=tau,
+                      q_scale=layer.q_scale, k_scale=layer.k_scale, v_scale=layer.v_scale)
+    layer.out = pf.out
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pf.pool()
+        if ev is not None:
+            ev[1].record()
+        pf.select()
+        if ev is not None:
+            ev[2].record()
+        pf.attend()
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    st = {"pool": [], "select": [], "attention": []}
+    for ev in evs:
+        st["pool"].append(ev[0].elapsed_time(ev[1]))
+        st["select"].append(ev[1].elapsed_time(ev[2]))
+        st["attention"].append(ev[2].elapsed_time(ev[3]))
+    stage_ms = {k: float(np.mean(v)) for k, v in st.items()}
+    ms_step = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    counts = pf.ws.counts().cpu().numpy()
+    L, B, d, Hq, Hkv = cfg.seq_len, cfg.block_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    nb = cfg.num_blocks
+    pairs = kept_pairs(counts, L, B)
+    flops = 4.0 * d * pairs
+    density = float(counts.sum()) / (Hq * nb * (nb + 1) / 2)
+    esz = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.dtype]
+    mfma_path = cfg.dtype == "bf16" and d == 128 and B == 128
+    pool_bytes = (L * (Hq + Hkv) * d * esz + (Hq + Hkv) * nb * d * 4
+                  + ((L * Hkv * d * esz + Hkv * d * nb * B * 2) if mfma_path else 0))
+    sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2
+    attn_tflops = flops / (stage_ms["attention"] * 1e-3) / 1e12
+    peak = PEAK["fp8"] if cfg.dtype == "fp8" else PEAK["bf16"]
+    wl = cfg.name + f"_tau{tau:g}"
+    traffic = measured_traffic(wl)
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "ms_per_layer": round(ms_step, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; sink / vertical / slash structure, RoPE theta 5e5)",
+        "config": {"workload": wl, "seq_len": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "block_size": B, "tau": tau, "dtype": cfg.dtype,
+                   "batch": 1},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "density": round(density, 5),
+        "kept_tflop": round(flops / 1e12, 4),
+        "attention_tflops": round(attn_tflops, 2),
+        "pool_gbs": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
+        "pool_hbm_frac": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK["hbm_gbs"], 4),
+        "select_tflops_fp32": round(sel_flops / (stage_ms["select"] * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
+        idx = pf.ws.indices()
+        tri = lambda h, i: h * (nb * (nb + 1) // 2) + i * (i + 1) // 2  # noqa: E731
+
+        def lists_gpu(h, i):
+            o = tri(h, i)
+            return idx[o:o + int(counts[h, i])].cpu().numpy()
+
+        res["cpu_baseline"] = cpu_baseline(layer, lists_gpu, counts, cfg, tau, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

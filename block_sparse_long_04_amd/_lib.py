@@ -1,0 +1,276 @@
+"""ctypes binding of libflashprefill.so (argument marshalling only).
+
+Every step of the computation runs in the HIP library; this module only turns
+torch tensors into the fp_problem struct of include/flashprefill.h (device
+pointers, element strides, dtype, scales), hands over torch's current HIP
+stream, and allocates the caller-owned workspace and output with torch.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libflashprefill.so")
+
+FP_F32, FP_BF16, FP_FP8_E4M3 = 0, 1, 2
+FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP = 0, -1, -2, -3, -4
+
+EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_sparse_prefill",
+            "fp_strerror")
+
+
+class FpProblem(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("seq_len", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("v_stride_tok", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+        ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("sm_scale", ctypes.c_float), ("threshold", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+    ]
+
+
+class FpWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("q_pool", "k_pool", "row_max", "counts", "indices", "v_t", "total")]
+
+
+class FlashPrefillError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once.  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m block_sparse_long_04_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, W = ctypes.POINTER(FpProblem), ctypes.POINTER(FpWsLayout)
+    lib.fp_workspace_layout.argtypes = [P, W]
+    lib.fp_workspace_layout.restype = ctypes.c_int
+    for name in ("fp_block_pool", "fp_block_select", "fp_sparse_prefill"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    lib.fp_strerror.argtypes = [ctypes.c_int]
+    lib.fp_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().fp_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != FP_OK:
+        raise FlashPrefillError(code, where)
+
+
+# ----------------------------------------------------------------------------
+# Raw entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+
+def fp_workspace_layout(prob: FpProblem) -> FpWsLayout:
+    lay = FpWsLayout()
+    _check(load_library().fp_workspace_layout(ctypes.byref(prob), ctypes.byref(lay)),
+           "fp_workspace_layout")
+    return lay
+
+
+def fp_block_pool(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_block_pool(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
+           "fp_block_pool")
+
+
+def fp_block_select(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_block_select(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
+           "fp_block_select")
+
+
+def fp_sparse_prefill(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_sparse_prefill(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
+           "fp_sparse_prefill")
+
+
+# ----------------------------------------------------------------------------
+# torch-facing helpers
+# ----------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FP_F32
+    if t.dtype == torch.bfloat16:
+        return FP_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_problem(q, k, v, out, block_size: int, threshold: float, sm_scale: float = 0.0,
+                 q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0,
+                 seq_len: Optional[int] = None, num_q_heads: Optional[int] = None,
+                 num_kv_heads: Optional[int] = None, head_dim: Optional[int] = None,
+                 dtype: Optional[int] = None) -> FpProblem:
+    """fp_problem for [L, H, d] tensors (any of them may be None: pointer 0;
+    shapes then come from the keyword overrides)."""
+    p = FpProblem()
+    ref_q = q if q is not None else None
+    p.q = q.data_ptr() if q is not None else 0
+    p.k = k.data_ptr() if k is not None else 0
+    p.v = v.data_ptr() if v is not None else 0
+    p.out = out.data_ptr() if out is not None else 0
+    p.seq_len = seq_len if seq_len is not None else ref_q.shape[0]
+    p.num_q_heads = num_q_heads if num_q_heads is not None else ref_q.shape[1]
+    p.num_kv_heads = num_kv_heads if num_kv_heads is not None else k.shape[1]
+    p.head_dim = head_dim if head_dim is not None else ref_q.shape[2]
+    p.block_size = block_size
+
+    def strides(t, H, d):
+        if t is None:  # contiguous default
+            return H * d, d
+        assert t.stride(2) == 1, "last dim must be contiguous"
+        return t.stride(0), t.stride(1)
+
+    p.q_stride_tok, p.q_stride_head = strides(q, p.num_q_heads, p.head_dim)
+    p.k_stride_tok, p.k_stride_head = strides(k, p.num_kv_heads, p.head_dim)
+    p.v_stride_tok, p.v_stride_head = strides(v, p.num_kv_heads, p.head_dim)
+    p.o_stride_tok, p.o_stride_head = strides(out, p.num_q_heads, p.head_dim)
+    p.dtype = dtype if dtype is not None else _dtype_code(q)
+    p.q_scale, p.k_scale, p.v_scale = q_scale, k_scale, v_scale
+    p.sm_scale = sm_scale
+    p.threshold = threshold
+    p.causal = 1
+    return p
+
+
+@dataclass
+class Workspace:
+    """Caller-owned workspace (a torch uint8 device tensor) plus typed views of
+    its sections (see fp_ws_layout)."""
+
+    buf: "object"
+    layout: FpWsLayout
+    nb: int
+    Hq: int
+    Hkv: int
+    d: int
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def _view(self, off, count, dtype):
+        import torch
+        esz = torch.empty((), dtype=dtype).element_size()
+        return self.buf[off: off + count * esz].view(dtype)
+
+    def q_pool(self):
+        import torch
+        return self._view(self.layout.q_pool, self.Hq * self.nb * self.d, torch.float32).view(
+            self.Hq, self.nb, self.d)
+
+    def k_pool(self):
+        import torch
+        return self._view(self.layout.k_pool, self.Hkv * self.nb * self.d, torch.float32).view(
+            self.Hkv, self.nb, self.d)
+
+    def row_max(self):
+        import torch
+        return self._view(self.layout.row_max, self.Hq * self.nb, torch.float32).view(self.Hq, self.nb)
+
+    def counts(self):
+        import torch
+        return self._view(self.layout.counts, self.Hq * self.nb, torch.int32).view(self.Hq, self.nb)
+
+    def indices(self):
+        import torch
+        return self._view(self.layout.indices, self.Hq * self.nb * (self.nb + 1) // 2, torch.int32)
+
+
+def alloc_workspace(prob: FpProblem, device) -> Workspace:
+    import torch
+    lay = fp_workspace_layout(prob)
+    buf = torch.empty(max(int(lay.total), 256), dtype=torch.uint8, device=device)
+    nb = (prob.seq_len + prob.block_size - 1) // prob.block_size
+    return Workspace(buf, lay, nb, prob.num_q_heads, prob.num_kv_heads, prob.head_dim)
+
+
+def current_stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Prefill:
+    """One layer's prefill problem bound to tensors: the three C-ABI calls on
+    torch's current stream.  Inputs q [L,Hq,d], k/v [L,Hkv,d] on one device
+    (fp32, bf16 or float8_e4m3fn); out is allocated [L,Hq,d] (fp32 for fp32
+    inputs, bf16 otherwise) unless given."""
+
+    def __init__(self, q, k, v, block_size: int = 128, threshold: float = 0.1,
+                 sm_scale: float = 0.0, q_scale: float = 1.0, k_scale: float = 1.0,
+                 v_scale: float = 1.0, out=None):
+        import torch
+        if not q.is_cuda:
+            raise ValueError("q/k/v must be device tensors")
+        if out is None:
+            odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+            out = torch.empty(q.shape, dtype=odt, device=q.device)
+        self.q, self.k, self.v, self.out = q, k, v, out
+        self.prob = make_problem(q, k, v, out, block_size, threshold, sm_scale,
+                                 q_scale, k_scale, v_scale)
+        self.ws = alloc_workspace(self.prob, q.device)
+        self.device = q.device
+
+    def stream(self) -> int:
+        return current_stream(self.device)
+
+    def pool(self):
+        fp_block_pool(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def select(self):
+        fp_block_select(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def attend(self):
+        fp_sparse_prefill(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def run(self):
+        self.pool()
+        self.select()
+        self.attend()
+        return self.out
+
+
+def prefill(q, k, v, threshold: float = 0.1, block_size: int = 128, **kw):
+    """Block-sparse causal prefill of one layer; returns (out, Prefill)."""
+    pf = Prefill(q, k, v, block_size=block_size, threshold=threshold, **kw)
+    return pf.run(), pf
+
+
+def default_sm_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

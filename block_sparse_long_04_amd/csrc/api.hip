@@ -1,0 +1,188 @@
+// C ABI of the block-sparse prefill library: argument checks, workspace
+// carving and stream-ordered launches.  Declarations and the meaning of every
+// argument are in include/flashprefill.h.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBlocks = 16384;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int elem_size(int dtype) { return dtype == FP_F32 ? 4 : (dtype == FP_BF16 ? 2 : 1); }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Non-overlap of an output [L][H][d] view with element strides (st, sh).
+bool out_view_ok(int64_t st, int64_t sh, int L, int H, int d) {
+  if (st <= 0 || sh <= 0) return false;
+  const bool tok_major = sh >= d && (L == 1 || st >= (int64_t)H * sh);
+  const bool head_major = st >= d && (H == 1 || sh >= (int64_t)L * st);
+  return tok_major || head_major;
+}
+
+// Shape/scalar checks common to every entry point (pointers are checked by
+// each entry point for the tensors it touches).
+int check_problem(const fp_problem* p, FpDims* dm) {
+  if (!p) return FP_ERR_INVALID;
+  if (p->seq_len < 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0 ||
+      p->block_size <= 0)
+    return FP_ERR_INVALID;
+  if (p->num_q_heads % p->num_kv_heads != 0) return FP_ERR_INVALID;
+  if (p->dtype != FP_F32 && p->dtype != FP_BF16 && p->dtype != FP_FP8_E4M3) return FP_ERR_INVALID;
+  if (isnan(p->threshold) || p->threshold < 0.f || p->threshold > 1.f) return FP_ERR_INVALID;
+  if (isnan(p->sm_scale) || isinf(p->sm_scale)) return FP_ERR_INVALID;
+  if (p->dtype == FP_FP8_E4M3) {
+    const float sc[3] = {p->q_scale, p->k_scale, p->v_scale};
+    for (float s : sc)
+      if (!(s > 0.f) || isinf(s)) return FP_ERR_INVALID;
+  }
+  if (p->causal != 1) return FP_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return FP_ERR_UNSUPPORTED;
+  if (p->block_size != 64 && p->block_size != 128) return FP_ERR_UNSUPPORTED;
+  const int64_t nb = ((int64_t)p->seq_len + p->block_size - 1) / p->block_size;
+  if (nb > kMaxBlocks) return FP_ERR_UNSUPPORTED;
+  const int es = elem_size(p->dtype);
+  const int64_t st[6] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok,
+                         p->k_stride_head, p->v_stride_tok, p->v_stride_head};
+  for (int64_t s : st)
+    if (s <= 0 || (s * es) % 16 != 0) return FP_ERR_INVALID;
+  const int oes = p->dtype == FP_F32 ? 4 : 2;
+  if (!out_view_ok(p->o_stride_tok, p->o_stride_head, p->seq_len, p->num_q_heads, p->head_dim) ||
+      (p->o_stride_tok * oes) % 16 != 0 || (p->o_stride_head * oes) % 16 != 0)
+    return FP_ERR_INVALID;
+  dm->L = p->seq_len;
+  dm->Hq = p->num_q_heads;
+  dm->Hkv = p->num_kv_heads;
+  dm->d = p->head_dim;
+  dm->B = p->block_size;
+  dm->nb = (int)nb;
+  return FP_OK;
+}
+
+void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {
+  const size_t nb = (size_t)dm.nb;
+  size_t off = 0;
+  w->q_pool = off;
+  off = align_up(off + (size_t)dm.Hq * nb * dm.d * sizeof(float));
+  w->k_pool = off;
+  off = align_up(off + (size_t)dm.Hkv * nb * dm.d * sizeof(float));
+  w->row_max = off;
+  off = align_up(off + (size_t)dm.Hq * nb * sizeof(float));
+  w->counts = off;
+  off = align_up(off + (size_t)dm.Hq * nb * sizeof(int));
+  w->indices = off;
+  off = align_up(off + (size_t)dm.Hq * (nb * (nb + 1) / 2) * sizeof(int));
+  w->v_t = off;
+  const bool mfma = p->dtype != FP_F32 && dm.d == 128 && dm.B == 128;
+  if (mfma) off = align_up(off + (size_t)dm.Hkv * dm.d * nb * dm.B * sizeof(uint16_t));
+  w->total = off;
+}
+
+bool use_mfma(const fp_problem* p, const FpDims& dm) {
+  return p->dtype == FP_BF16 && dm.d == 128 && dm.B == 128;
+}
+
+int check_ws(const fp_problem* p, const FpDims& dm, void* ws, size_t bytes, fp_ws_layout* w) {
+  layout_of(p, dm, w);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 || bytes < w->total)
+    return FP_ERR_WORKSPACE;
+  return FP_OK;
+}
+
+float eff_sm_scale(const fp_problem* p) {
+  return p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / sqrt((double)p->head_dim));
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp_workspace_layout(const fp_problem* p, fp_ws_layout* layout) {
+  FpDims dm;
+  const int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (!layout) return FP_ERR_INVALID;
+  layout_of(p, dm, layout);
+  return FP_OK;
+}
+
+int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (dm.L == 0) return FP_OK;
+  if (!p->q || !p->k || !aligned16(p->q) || !aligned16(p->k)) return FP_ERR_INVALID;
+  if (use_mfma(p, dm) && (!p->v || !aligned16(p->v))) return FP_ERR_INVALID;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = fpk_launch_pool(*p, dm, at<float>(workspace, w.q_pool),
+                                 at<float>(workspace, w.k_pool), st);
+  if (e == hipSuccess && use_mfma(p, dm)) e = fpk_launch_vtrans(*p, dm, at<uint16_t>(workspace, w.v_t), st);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_block_select(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (dm.L == 0) return FP_OK;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const float lt = p->threshold == 0.f ? -INFINITY : (float)log((double)p->threshold);
+  const hipError_t e =
+      fpk_launch_select(dm, at<float>(workspace, w.q_pool), at<float>(workspace, w.k_pool),
+                        eff_sm_scale(p), lt, at<float>(workspace, w.row_max),
+                        at<int>(workspace, w.counts), at<int>(workspace, w.indices),
+                        (hipStream_t)stream);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (dm.L == 0) return FP_OK;
+  if (!p->q || !p->k || !p->v || !p->out || !aligned16(p->q) || !aligned16(p->k) ||
+      !aligned16(p->v) || !aligned16(p->out))
+    return FP_ERR_INVALID;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const hipStream_t st = (hipStream_t)stream;
+  const float sc = eff_sm_scale(p);
+  const int* counts = at<int>(workspace, w.counts);
+  const int* indices = at<int>(workspace, w.indices);
+  hipError_t e;
+  if (use_mfma(p, dm)) {
+    e = fpk_launch_attn_mfma(*p, dm, counts, indices, at<uint16_t>(workspace, w.v_t), sc, st);
+  } else {
+    e = fpk_launch_attn_generic(*p, dm, counts, indices, sc, st);
+  }
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+const char* fp_strerror(int code) {
+  switch (code) {
+    case FP_OK: return "ok";
+    case FP_ERR_INVALID: return "invalid argument (pointer, shape, stride, alignment, scale or threshold)";
+    case FP_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, block_size, causal or block count)";
+    case FP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

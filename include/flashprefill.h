@@ -1,0 +1,134 @@
+/*
+ * flashprefill.h -- C ABI of the block-sparse causal prefill library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the FlashPrefill prefill attention of one layer:
+ *   1. mean-pool Q and K into one proxy vector per block of B tokens
+ *      ("FlashPrefill: Instantaneous Pattern Discovery for Ultra-Fast
+ *      Long-Context Prefilling", skill page: "Architecture Overview",
+ *      block-level proxy computation, and the Stage 1 code of
+ *      "Implementation Steps");
+ *   2. score every causal proxy block pair, S[h,i,j] = Qbar[h,i].Kbar[g,j] *
+ *      sm_scale (same Stage 1 code; "Core Concept" item 2);
+ *   3. keep key block j of query block i when exp(S[h,i,j] - m[h,i]) >= tau,
+ *      m being the single-pass row maximum; the diagonal block is always kept
+ *      ("Core Concept" item 3; the FlashPrefill abstract: dynamic thresholding
+ *      without sorting or accumulation);
+ *   4. compact the kept key blocks of each (head, query block) into an
+ *      ascending index list ("Architecture Overview": physical index jumping);
+ *   5. exact softmax attention of every query over the keys of its listed
+ *      blocks, causal inside the diagonal block, with grouped-query heads
+ *      (kv head = q head / (Hq/Hkv)); FP8 inputs as in the FlashPrefill V2
+ *      abstract ("FlashPrefill V2: Block-Sparse Prefill Attention for
+ *      Long-Context LLM Serving").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named q, k, v, out and the workspace are DEVICE pointers,
+ *     allocated and owned by the caller.  The library never allocates, frees
+ *     or keeps them.  The fp_problem struct itself is host memory, read during
+ *     the call only.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  No call synchronises the host.  A kernel fault surfaces at the
+ *     caller's next synchronisation.
+ *   - All argument checks run on the host before any launch.  A call that
+ *     returns an error has launched nothing and written nothing.
+ *   - Tensors are [token, head, dim] views given by element strides; the
+ *     last (dim) axis must be contiguous.  Every base pointer must be 16-byte
+ *     aligned and every stride a multiple of 16 bytes.
+ *   - Functions are re-entrant; the library holds no per-call global state.
+ *     Two calls that share a workspace must be ordered on one stream.
+ *   - seq_len == 0 is an empty problem: every call returns FP_OK and launches
+ *     nothing.
+ */
+#ifndef FLASHPREFILL_H
+#define FLASHPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k and v.  out is fp32 for FP_F32 and bf16 otherwise.
+ * FP_FP8_E4M3 is the OCP e4m3fn format (bias 7, no infinities, max 448),
+ * dequantised as code * scale with one scale per tensor. */
+typedef enum fp_dtype { FP_F32 = 0, FP_BF16 = 1, FP_FP8_E4M3 = 2 } fp_dtype;
+
+/* Return codes. */
+enum {
+  FP_OK = 0,
+  FP_ERR_INVALID = -1,     /* null pointer, bad shape/stride/alignment, tau outside [0,1] or NaN,
+                              non-finite or non-positive scale, Hq not a multiple of Hkv */
+  FP_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size not 64/128, causal != 1,
+                              more than 16384 blocks */
+  FP_ERR_WORKSPACE = -3,   /* workspace null, misaligned (256 B) or smaller than fp_workspace_layout().total */
+  FP_ERR_HIP = -4          /* the HIP runtime refused a launch */
+};
+
+/* One layer's prefill problem (batch 1). */
+typedef struct fp_problem {
+  const void* q;   /* [seq_len, num_q_heads, head_dim] */
+  const void* k;   /* [seq_len, num_kv_heads, head_dim] */
+  const void* v;   /* [seq_len, num_kv_heads, head_dim] */
+  void* out;       /* [seq_len, num_q_heads, head_dim], written by fp_sparse_prefill only */
+  int32_t seq_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads; /* num_q_heads % num_kv_heads == 0 (grouped-query attention) */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t block_size;   /* B: 64 or 128 tokens per block (pooling, selection and attention tile) */
+  int64_t q_stride_tok, q_stride_head; /* element strides */
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t o_stride_tok, o_stride_head; /* out must not overlap itself */
+  int32_t dtype;        /* fp_dtype */
+  float q_scale, k_scale, v_scale; /* fp8 dequantisation scales; ignored (taken as 1) otherwise */
+  float sm_scale;       /* softmax / proxy-score scale; <= 0 selects 1/sqrt(head_dim) */
+  float threshold;      /* tau in [0, 1]: keep block j iff exp(S_ij - m_i) >= tau; 0 keeps every causal block */
+  int32_t causal;       /* must be 1: causal prefill */
+} fp_problem;
+
+/* Byte offsets of the workspace sections (each 256-byte aligned) and the
+ * total size.  nb = ceil(seq_len / block_size).
+ *   q_pool  float [num_q_heads][nb][head_dim]   pooled query proxies (scaled by q_scale)
+ *   k_pool  float [num_kv_heads][nb][head_dim]  pooled key proxies (scaled by k_scale)
+ *   row_max float [num_q_heads][nb]             m[h,i] = max_{j<=i} S[h,i,j]
+ *   counts  int32 [num_q_heads][nb]             kept blocks of row (h,i)
+ *   indices int32, triangular: row (h,i) starts at h*nb*(nb+1)/2 + i*(i+1)/2, holds
+ *           counts[h][i] ascending key-block indices (capacity i+1)
+ *   v_t     bf16 [num_kv_heads][head_dim][nb*block_size]  V transposed per kv head, zero past
+ *           seq_len (written by fp_block_pool; zero-length for fp32 inputs)
+ * The layout is part of the ABI: a caller may read the selection, or write
+ * its own counts/indices (ascending, each list ending with its diagonal
+ * block i) before fp_sparse_prefill to run attention on a given mask. */
+typedef struct fp_ws_layout {
+  size_t q_pool, k_pool, row_max, counts, indices, v_t, total;
+} fp_ws_layout;
+
+/* Host only, launches nothing: validates *p (pointers may be NULL here) and
+ * fills *layout.  Returns FP_OK or an error code. */
+int fp_workspace_layout(const fp_problem* p, fp_ws_layout* layout);
+
+/* Step 1.  Reads q and k and writes the q_pool and k_pool sections.  For
+ * bf16 inputs with head_dim 128 and block_size 128 it also reads v and writes
+ * the v_t section (the key-contiguous V layout the matrix-core attention
+ * reads), so that stage streams V once here rather than inside the attention
+ * loop. */
+int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Steps 2-4.  Reads q_pool, k_pool; writes row_max, counts and indices.  The
+ * block score matrix is never stored. */
+int fp_block_select(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 5.  Reads q, k, v (or v_t, written by fp_block_pool), counts and
+ * indices; writes out.  Must follow fp_block_pool on the same workspace. */
+int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text of a return code. */
+const char* fp_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHPREFILL_H */

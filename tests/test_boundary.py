@@ -1,0 +1,156 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any launch (every
+call here returns an error code without touching a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_long_04_amd as fp
+from block_sparse_long_04_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashprefill.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fp_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fp.load_library()
+    names = header_functions()
+    assert names == sorted(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header(tmp_path):
+    # offsets and sizes of the ctypes mirrors equal what a C compiler makes of
+    # the header
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "flashprefill.h"',
+             'int main(void) {']
+    for struct, cls in (("fp_problem", fp.FpProblem), ("fp_ws_layout", fp.FpWsLayout)):
+        lines.append(f'printf("{struct} %zu\\n", sizeof({struct}));')
+        for name, _ in cls._fields_:
+            lines.append(f'printf("{struct}.{name} %zu\\n", offsetof({struct}, {name}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(ln.split() for ln in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                    check=True).stdout.splitlines())
+    for struct, cls in (("fp_problem", fp.FpProblem), ("fp_ws_layout", fp.FpWsLayout)):
+        assert int(got[struct]) == ctypes.sizeof(cls)
+        for name, _ in cls._fields_:
+            assert int(got[f"{struct}.{name}"]) == getattr(cls, name).offset, name
+
+
+def prob(**kw):
+    base = dict(seq_len=1000, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=fp.FP_BF16)
+    base.update({k: v for k, v in kw.items() if k in base})
+    p = fp.make_problem(None, None, None, None, kw.get("block_size", 128), kw.get("threshold", 0.1),
+                        **base)
+    for k, v in kw.items():
+        if k not in base and k not in ("block_size", "threshold"):
+            setattr(p, k, v)
+    return p
+
+
+def test_workspace_layout_sizes_and_alignment():
+    p = prob()
+    lay = fp.fp_workspace_layout(p)
+    nb = 8
+    assert lay.q_pool == 0
+    assert lay.k_pool == 8 * nb * 128 * 4
+    offs = [lay.q_pool, lay.k_pool, lay.row_max, lay.counts, lay.indices, lay.v_t, lay.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.indices - lay.counts >= 8 * nb * 4
+    assert lay.v_t - lay.indices >= 8 * nb * (nb + 1) // 2 * 4
+    assert lay.total - lay.v_t == 2 * 128 * nb * 128 * 2  # V^T in bf16
+    lay32 = fp.fp_workspace_layout(prob(dtype=fp.FP_F32))
+    assert lay32.total == lay32.v_t  # no V^T for fp32 inputs
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("threshold", float("nan"), fp.FP_ERR_INVALID),
+    ("threshold", -0.01, fp.FP_ERR_INVALID),
+    ("threshold", 1.5, fp.FP_ERR_INVALID),
+    ("num_kv_heads", 3, fp.FP_ERR_INVALID),
+    ("num_q_heads", 0, fp.FP_ERR_INVALID),
+    ("seq_len", -1, fp.FP_ERR_INVALID),
+    ("head_dim", 96, fp.FP_ERR_UNSUPPORTED),
+    ("block_size", 32, fp.FP_ERR_UNSUPPORTED),
+    ("causal", 0, fp.FP_ERR_UNSUPPORTED),
+    ("dtype", 7, fp.FP_ERR_INVALID),
+    ("q_stride_head", 100, fp.FP_ERR_INVALID),  # 200 bytes: not a multiple of 16
+    ("o_stride_tok", 128, fp.FP_ERR_INVALID),   # output rows of different heads overlap
+    ("sm_scale", float("inf"), fp.FP_ERR_INVALID),
+    ("seq_len", 16385 * 128, fp.FP_ERR_UNSUPPORTED),
+])
+def test_invalid_problem_rejected(field, value, code):
+    p = prob()
+    setattr(p, field, value)
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_workspace_layout(p)
+    assert e.value.code == code
+
+
+def test_fp8_scales_validated():
+    p = prob(dtype=fp.FP_FP8_E4M3)
+    p.q_scale = 0.0
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_workspace_layout(p)
+    assert e.value.code == fp.FP_ERR_INVALID
+    p.q_scale = float("inf")
+    with pytest.raises(fp.FlashPrefillError):
+        fp.fp_workspace_layout(p)
+
+
+def test_entry_points_reject_before_launch():
+    # Host-side errors come back before any HIP call: null tensors, null or
+    # misaligned or short workspace.  Fake addresses are never dereferenced.
+    p = prob()
+    lay = fp.fp_workspace_layout(p)
+    fake = 1 << 20
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_block_pool(p, fake, lay.total, 0)  # q/k are NULL
+    assert e.value.code == fp.FP_ERR_INVALID
+    p.q, p.k, p.v, p.out = fake, fake, fake, fake
+    for fn in (fp.fp_block_pool, fp.fp_block_select, fp.fp_sparse_prefill):
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fn(p, 0, lay.total, 0)
+        assert e.value.code == fp.FP_ERR_WORKSPACE
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fn(p, fake + 16, lay.total, 0)
+        assert e.value.code == fp.FP_ERR_WORKSPACE
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fn(p, fake, lay.total - 1, 0)
+        assert e.value.code == fp.FP_ERR_WORKSPACE
+    p.q = fake + 8  # misaligned tensor
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_block_pool(p, fake, lay.total, 0)
+    assert e.value.code == fp.FP_ERR_INVALID
+
+
+def test_empty_problem_is_a_no_op():
+    p = prob(seq_len=0)
+    lay = fp.fp_workspace_layout(p)
+    for fn in (fp.fp_block_pool, fp.fp_block_select, fp.fp_sparse_prefill):
+        fn(p, 0, 0, 0)  # nothing launched, nothing read
+    assert lay.total == 0
+
+
+def test_strerror_texts():
+    for code in (0, -1, -2, -3, -4):
+        assert fp.strerror(code)
+    assert "unknown" in fp.strerror(12345)
