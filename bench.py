@@ -281,6 +281,9 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "density": round(density, 5),
         "kept_tflop": round(flops / 1e12, 4),
+        "row_counts": {"mean": round(float(counts.mean()), 2), "max": int(counts.max()),
+                       "p50": float(np.percentile(counts, 50)),
+                       "p99": float(np.percentile(counts, 99))},
         "attention_tflops": round(attn_tflops, 2),
         "pool_gbs": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
         "pool_hbm_frac": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK["hbm_gbs"], 4),

@@ -1,40 +1,48 @@
 // Step 5 on the matrix cores: block-sparse causal attention with GQA over the
-// kept key blocks, bf16 inputs (e4m3fn variant in attn_fp8.hip), head_dim 128,
-// block 128.
+// kept key blocks, bf16 inputs, head_dim 128, block 128.
 //
 // FlashPrefill skill page, "Architecture Overview" (physical index jumping:
 // only the listed key blocks are visited) and "Implementation Steps" (the
-// final stage is block-sparse attention over the identified blocks); GQA per
+// last stage is block-sparse attention over the identified blocks); GQA per
 // the FlashPrefill V2 abstract.
 //
-// One workgroup = one (q head h, query block i), four waves of 32 query rows.
+// One workgroup = one (q head h, query block i), 8 waves.  Wave w owns query
+// rows 32*(w%4) .. +31 and key half kh = w/4 (keys 64kh .. 64kh+63 of every
+// kept block); the two halves keep separate online-softmax states and are
+// merged through LDS at the end.  Two waves per SIMD let one wave's softmax
+// (VALU) run under the other's matrix-core work.
+//
 // Per kept key block j (ascending list, the diagonal last):
 //   * the K tile [128 keys][128 dims] and the V^T tile [128 dims][128 keys]
-//     are staged in LDS (16-byte chunks, chunk index XOR (row & 15) so the
-//     matrix-core operand reads are bank-conflict free);
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (four 32-key sub-tiles, eight
-//     16-wide steps over the head dimension).  Computing the transpose puts
-//     one query per lane column, so each lane owns 64 of its query's 128
-//     logits and the other half sits in lane ^ 32: softmax statistics need a
-//     single cross-lane exchange.  The K rows are fed in the permuted order
-//     that makes those 64 logits come out as contiguous 8-key runs, which are
-//     exactly the B operand of the next product;
-//   * online softmax in the exp2 domain (running max and sum per query);
-//   * O^T += V^T P^T, P packed to bf16 straight from the S^T registers.
-// The causal mask is applied only on the diagonal block.  The final 1/l and
-// the V dequantisation scale are applied once at the end.
+//     travel global -> LDS with global_load_lds_dwordx4 (no registers), double
+//     buffered: the next block's tiles are in flight while this one computes.
+//     Rows are 16 chunks of 16 B stored at chunk ^ f(row), f(r) = (r & 15) ^
+//     (((r >> 3) & 1) << 2), so the operand reads below hit distinct banks;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: two 32-key sub-tiles, eight
+//     16-wide steps over the head dimension.  A lane column is one query, so
+//     a lane holds 32 of its query's logits and lane ^ 32 the rest.  K rows
+//     are fed in the order pm(m) (bits 2 and 3 of m swapped), which makes
+//     each lane's logits contiguous 8-key runs: the B operand of P.V as is;
+//   * online softmax in the exp2 domain with a lazy maximum: the running max
+//     is raised (and O, l rescaled) only when a tile's max exceeds it by more
+//     than 8 (P <= 2^8 stays exact enough in bf16 and cannot overflow fp32);
+//   * O^T += V^T P^T, P packed to bf16 from the S^T registers.
+// The causal mask is applied on the diagonal block only.  1/l and the V
+// dequantisation scale are applied once, after the merge.
 //
 // Work order: heavy (late) query blocks first; within every run of 8*G
 // consecutive workgroup ids, the G heads of one kv group at one query block
-// get ids that the hardware dispatches to the same XCD (ids are dealt to the
-// 8 XCDs round-robin), so a K/V tile fetched for one head is found in that
-// XCD's L2 by the other heads of its group.
+// get ids the hardware deals to the same XCD (ids go round-robin over the 8
+// XCDs), so a K/V tile fetched for one head is found in that XCD's L2 by the
+// other heads of its group.  The group-to-XCD assignment rotates with the
+// query block so that no XCD is left with one group's whole workload.
 #include "common.h"
 
 namespace {
 
 using fpk::bf16x8;
 using fpk::floatx16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
   const uint8_t* q;
@@ -45,9 +53,12 @@ struct AttnArgs {
   const int* indices;
   int64_t q_st, q_sh, k_st, k_sh, o_st, o_sh;
   int L, Hq, Hkv, nb, Lpad;
-  float scale_log2;  // sm_scale * log2(e)
+  float scale_log2;  // sm_scale * log2(e) (times q_scale * k_scale for e4m3 inputs)
   float out_scale;
 };
+
+constexpr int kTileU4 = 128 * 16;  // one 128 x 256 B tile in uint4
+constexpr float kLazy = 8.0f;      // lazy-max slack in log2 units
 
 __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int& h, int& i) {
   const int G = Hq / Hkv;
@@ -56,9 +67,12 @@ __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int&
   const int full = (total / chunk) * chunk;
   int p, slot;
   if (bid < full) {
+    // run `sup` of 8*G ids: XCD x (= id % 8) gets (row, group) pair
+    // sup*8 + (x + sup) % 8 with its G heads; the rotation spreads every kv
+    // group over all XCDs, so per-group differences in kept work even out.
     const int sup = bid / chunk;
     const int r = bid - sup * chunk;
-    p = sup * 8 + (r & 7);
+    p = sup * 8 + (((r & 7) + sup) & 7);
     slot = r >> 3;
   } else {
     p = bid / G;
@@ -69,9 +83,198 @@ __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int&
   h = (p - row * Hkv) * G + slot;
 }
 
-__global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
-  __shared__ uint4 sK[128 * 16];  // [key][16 chunks], swizzled
-  __shared__ uint4 sV[128 * 16];  // [dim][16 chunks of 8 keys], swizzled
+__device__ __forceinline__ int swz(int row) { return (row & 15) ^ (((row >> 3) & 1) << 2); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+struct WaveState {
+  floatx16 o[4];
+  float m;  // lazy running max (log2 domain)
+  float l;  // this lane's partial row sum
+};
+
+// Softmax statistics of one tile's logits: causal mask on the diagonal block,
+// row max, and the lazy raise of the running max (rescaling O and l).
+__device__ __forceinline__ void softmax_stats(floatx16* s, WaveState& ws, float c, bool diag,
+                                              int qg, int kh, int qi, int hh) {
+  if (diag) {
+    const int qrel = 32 * qg + qi;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int krel = 64 * kh + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (krel > qrel) s[kt][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mxs = mx * c;
+  if (__any(mxs > ws.m + kLazy)) {
+    const float m_new = fmaxf(ws.m, mxs);
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(ws.m - m_new);
+    ws.m = m_new;
+    ws.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) ws.o[dt] *= alpha;
+  }
+}
+
+// exp2 of one 32-key sub-tile into bf16 P (two 8-key runs); the row sum is
+// taken from the bf16 values themselves with v_dot2 against (1, 1), so l
+// normalises exactly the weights that enter P.V.
+__device__ __forceinline__ void exp_subtile(const floatx16& s, float c, float mu, float& l,
+                                            bf16x8& p0, bf16x8& p1) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(s[r] * c - mu);
+    if (r < 8) p0[r] = p;
+    else p1[r - 8] = p;
+  }
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    l = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p0[2 * e], p0[2 * e + 1]}, one, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p1[2 * e], p1[2 * e + 1]}, one, l, false);
+  }
+}
+
+// One pipelined step: S(n+1) = K(n+1) Q^T on the matrix cores interleaved
+// with the exponentials of tile n, then O += P(n) V(n) interleaved with the
+// rest of the exponentials.  sched_group_barrier pins the interleave (MFMA,
+// LDS read, a few VALU) so the in-order wave keeps both pipes busy.
+__device__ __forceinline__ void pipelined_step(const uint4* sKn, const uint4* sV,
+                                               const bf16x8* qf, const floatx16* s_cur,
+                                               floatx16* s_nxt, WaveState& ws, float c, int kh,
+                                               int qi, int hh, int pm) {
+  const float mu = ws.m == -INFINITY ? 0.0f : ws.m;
+  const int row0 = 64 * kh + pm;
+  const int row1 = row0 + 32;
+  const int x0 = swz(row0) ^ hh, x1 = swz(row1) ^ hh;
+  const uint4* k0 = sKn + row0 * 16;
+  const uint4* k1 = sKn + row1 * 16;
+  s_nxt[0] = (floatx16){0};
+  s_nxt[1] = (floatx16){0};
+  bf16x8 pb[4];
+  float l = ws.l;
+  // -- S(n+1): 16 MFMAs, the two sub-tile chains alternating
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&k0[(2 * st) ^ x0]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&k1[(2 * st) ^ x1]);
+    s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[st], s_nxt[0], 0, 0, 0);
+    s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[st], s_nxt[1], 0, 0, 0);
+  }
+  exp_subtile(s_cur[0], c, mu, l, pb[0], pb[1]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  }
+  // -- O += P V for this half's 64 keys, with the second sub-tile's exps
+  exp_subtile(s_cur[1], c, mu, l, pb[2], pb[3]);
+  const int xv = (8 * kh) ^ hh;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int drow = 32 * dt + qi;
+      const bf16x8 av =
+          *reinterpret_cast<const bf16x8*>(&sV[drow * 16 + ((2 * u) ^ xv ^ swz(drow))]);
+      ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[u], ws.o[dt], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  ws.l = l;
+}
+
+// S^T sub-tiles of this wave's 64 keys of one K tile (prologue only).
+__device__ __forceinline__ void qk_tile(const uint4* sK, const bf16x8* qf, floatx16* s, int kh,
+                                        int hh, int pm) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = (floatx16){0};
+    const int row = 64 * kh + 32 * kt + pm;
+    const int sw = swz(row);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sK[row * 16 + ((2 * st + hh) ^ sw)]);
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[st], s[kt], 0, 0, 0);
+    }
+  }
+}
+
+// Direct-to-LDS tile loads.  Wave w moves row quads 4w .. 4w+3 of a tile:
+// lane l fills slot l%16 of row 16w + 4e + l/16 with the global chunk
+// (l%16) ^ swz(row).  The per-lane byte offsets are fixed for the whole
+// workgroup; only the uniform tile base moves with the key block.
+struct TileLoader {
+  const uint8_t* kbase;  // K of kv head g
+  const uint8_t* vbase;  // V^T rows of kv head g
+  int64_t k_tile;        // bytes between consecutive key blocks of K
+  int64_t k_st;
+  uint32_t koff[4], voff[4];
+  int row[4], chunk[4];
+  int L;
+
+  __device__ __forceinline__ void init(const AttnArgs& a, int g, int w, int lane) {
+    kbase = a.k + (int64_t)g * a.k_sh * 2;
+    vbase = reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)g * 128 * a.Lpad * 2;
+    k_tile = (int64_t)128 * a.k_st * 2;
+    k_st = a.k_st;
+    L = a.L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      row[e] = 16 * w + 4 * e + (lane >> 4);
+      chunk[e] = (lane & 15) ^ swz(row[e]);
+      koff[e] = (uint32_t)(row[e] * a.k_st * 2 + chunk[e] * 16);
+      voff[e] = (uint32_t)((int64_t)row[e] * a.Lpad * 2 + chunk[e] * 16);
+    }
+  }
+  __device__ __forceinline__ void load_k(uint4* sK, int j, int w) const {
+    const uint8_t* base = kbase + (int64_t)j * k_tile;
+    if (j * 128 + 128 <= L) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_global_load_lds(base + koff[e], (lds_ptr_t)(sK + (4 * w + e) * 64), 16, 0, 0);
+    } else {  // ragged last block: rows past L repeat row L-1 (masked later)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = min(row[e], L - 1 - j * 128);
+        __builtin_amdgcn_global_load_lds(base + (int64_t)r * k_st * 2 + chunk[e] * 16,
+                                         (lds_ptr_t)(sK + (4 * w + e) * 64), 16, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void load_v(uint4* sV, int j, int w) const {
+    const uint8_t* base = vbase + (int64_t)j * 256;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      __builtin_amdgcn_global_load_lds(base + voff[e], (lds_ptr_t)(sV + (4 * w + e) * 64), 16, 0, 0);
+  }
+};
+
+#define FP_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70) /* vmcnt(0) */
+
+__global__ __launch_bounds__(512) void attn_bf16_d128_kernel(AttnArgs a) {
+  // K tile m lives in sK[m & 1], V^T tile m in sV[m & 1]; K runs one tile
+  // ahead of V because S(n+1) = K(n+1) Q^T is issued before P(n) V(n).
+  __shared__ uint4 sK0[kTileU4], sK1[kTileU4];
+  __shared__ uint4 sV0[kTileU4], sV1[kTileU4];
 
   int h, i;
   work_item(blockIdx.x, a.nb, a.Hq, a.Hkv, h, i);
@@ -79,14 +282,38 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int qg = w & 3;
+  const int kh = w >> 2;
   const int qi = lane & 31;
   const int hh = lane >> 5;
-  const int tq = i * 128 + w * 32 + qi;
+  const int tq = i * 128 + 32 * qg + qi;
+  const int pm = (qi & 0x13) | ((qi & 4) << 1) | ((qi & 8) >> 1);
+  const float c = a.scale_log2;
+
+  const int cnt = a.counts[(int64_t)h * a.nb + i];
+  const int* lst = a.indices + fpk::tri_offset(h, i, a.nb);
+
+  // The kept list is read 64 entries at a time into one VGPR (lane e holds
+  // entry base + e) and entries are taken with readlane: no per-tile memory
+  // wait, so in-flight tile prefetches are never drained for an index.
+  int win = lst[min(lane, cnt - 1)];
+  int wbase = 0;
+  auto entry = [&](int n) -> int {
+    if (n - wbase >= 64) {
+      wbase += 64;
+      win = lst[min(wbase + lane, cnt - 1)];
+    }
+    return __builtin_amdgcn_readlane(win, n - wbase);
+  };
+
+  TileLoader ld;
+  ld.init(a, g, w, lane);
 
   // B operand of S^T = K Q^T: lane holds Q[tq][16s + 8hh .. +7] for step s.
   bf16x8 qf[8];
   if (tq < a.L) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + tq * a.q_st + h * a.q_sh + 8 * hh;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)tq * a.q_st +
+                         (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   } else {
@@ -94,118 +321,96 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(AttnArgs a) {
     for (int s = 0; s < 8; ++s) qf[s] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
   }
 
-  floatx16 o[4];
+  // prologue: K(0), K(1), V(0), V(1) in; S(0); then K(2) on its way
+  int j0 = entry(0);
+  int j1 = cnt > 1 ? entry(1) : 0;
+  int j2 = cnt > 2 ? entry(2) : 0;
+  ld.load_k(sK0, j0, w);
+  ld.load_v(sV0, j0, w);
+  if (cnt > 1) {
+    ld.load_k(sK1, j1, w);
+    ld.load_v(sV1, j1, w);
+  }
+  WaveState ws;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = (floatx16){0};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int dt = 0; dt < 4; ++dt) ws.o[dt] = (floatx16){0};
+  ws.m = -INFINITY;
+  ws.l = 0.f;
+  FP_WAIT_VMEM();
+  __syncthreads();
+  floatx16 sA[2], sB[2];
+  qk_tile(sK0, qf, sA, kh, hh, pm);
+  __syncthreads();
+  if (cnt > 2) ld.load_k(sK0, j2, w);
 
-  const int cnt = a.counts[(int64_t)h * a.nb + i];
-  const int* lst = a.indices + fpk::tri_offset(h, i, a.nb);
-  // Output row m of the 32x32 tile sits in register 4*(m/8) + m%4 of lane
-  // half (m/4)&1; feeding key pm(m) = m with bits 2 and 3 swapped as row m
-  // makes register r of half hh hold key 16*(r/8) + 8*hh + r%8.
-  const int pm = (qi & 0x13) | ((qi & 4) << 1) | ((qi & 8) >> 1);
-  const int lc = tid & 15;   // tile-load chunk
-  const int lr = tid >> 4;   // tile-load row base
-
-  for (int n = 0; n < cnt; ++n) {
-    const int j = lst[n];
+  // Step n (tiles n and n+1 live in the S registers and K buffers):
+  //   mask/max/rescale of S(n); S(n+1) || exp(S(n)); O += P(n) V(n);
+  //   wait + barrier; prefetch K(n+3) into K(n+1)'s buffer, V(n+2) into V(n)'s.
+  // Two steps per trip so buffer and register roles are static.
+  for (int n = 0; n < cnt; n += 2) {
+    softmax_stats(sA, ws, c, j0 == i, qg, kh, qi, hh);
+    pipelined_step(sK1, sV0, qf, sA, sB, ws, c, kh, qi, hh, pm);
+    FP_WAIT_VMEM();
     __syncthreads();
     {
-      uint4 kv[8], vv[8];
-      const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + g * a.k_sh + lc * 8;
-      const uint16_t* vb = a.vt + ((int64_t)g * 128) * a.Lpad + (int64_t)j * 128 + lc * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = lr + 16 * e;
-        const int key = j * 128 + row;
-        kv[e] = key < a.L ? *reinterpret_cast<const uint4*>(kb + (int64_t)key * a.k_st)
-                          : make_uint4(0, 0, 0, 0);
-        vv[e] = *reinterpret_cast<const uint4*>(vb + (int64_t)row * a.Lpad);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = lr + 16 * e;
-        sK[row * 16 + (lc ^ (row & 15))] = kv[e];
-        sV[row * 16 + (lc ^ (row & 15))] = vv[e];
-      }
+      const int j3 = n + 3 < cnt ? entry(n + 3) : 0;
+      if (n + 3 < cnt) ld.load_k(sK1, j3, w);
+      if (n + 2 < cnt) ld.load_v(sV0, j2, w);
+      j0 = j1;
+      j1 = j2;
+      j2 = j3;
     }
+    if (n + 1 >= cnt) break;
+    softmax_stats(sB, ws, c, j0 == i, qg, kh, qi, hh);
+    pipelined_step(sK0, sV1, qf, sB, sA, ws, c, kh, qi, hh, pm);
+    FP_WAIT_VMEM();
     __syncthreads();
-
-    floatx16 s[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = (floatx16){0};
-      const int row = kt * 32 + pm;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sK[row * 16 + ((2 * st + hh) ^ (row & 15))]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[st], s[kt], 0, 0, 0);
-      }
-    }
-    if (j == i) {
-      const int qrel = w * 32 + qi;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int krel = kt * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-          if (krel > qrel) s[kt][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kt][r] * a.scale_log2 - m_new);
-        s[kt][r] = p;
-        l_run += p;
-      }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-
-    bf16x8 pb[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[u >> 1][8 * (u & 1) + e];
-
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int drow = dt * 32 + qi;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sV[drow * 16 + ((2 * u + hh) ^ (drow & 15))]);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[u], o[dt], 0, 0, 0);
-      }
+    {
+      const int j3 = n + 4 < cnt ? entry(n + 4) : 0;
+      if (n + 4 < cnt) ld.load_k(sK0, j3, w);
+      if (n + 3 < cnt) ld.load_v(sV1, j2, w);
+      j0 = j1;
+      j1 = j2;
+      j2 = j3;
     }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = a.out_scale / l_tot;
+  // merge the two key halves of each query group through LDS
+  float* mrg = reinterpret_cast<float*>(sK0);  // [qg][66][64] floats over sK0..sV1
+  if (kh == 1) {
+    float* dst = mrg + qg * 66 * 64;
+    dst[lane] = ws.m;
+    dst[64 + lane] = ws.l;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(2 + 16 * dt + r) * 64 + lane] = ws.o[dt][r];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float* src = mrg + qg * 66 * 64;
+  const float m1 = src[lane];
+  const float l1 = src[64 + lane] + src[64 + (lane ^ 32)];
+  const float l0 = ws.l + __shfl_xor(ws.l, 32);
+  const float m = fmaxf(ws.m, m1);
+  const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ws.m - m);
+  const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+  const float inv = a.out_scale / (l0 * a0 + l1 * a1);
   if (tq < a.L) {
-    uint16_t* op = a.out + tq * a.o_st + h * a.o_sh;
+    uint16_t* op = a.out + (int64_t)tq * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = dt * 32 + 8 * q4 + 4 * hh;
-        const uint32_t b0 = fpk::f32_to_bf16_bits(o[dt][4 * q4 + 0] * inv);
-        const uint32_t b1 = fpk::f32_to_bf16_bits(o[dt][4 * q4 + 1] * inv);
-        const uint32_t b2 = fpk::f32_to_bf16_bits(o[dt][4 * q4 + 2] * inv);
-        const uint32_t b3 = fpk::f32_to_bf16_bits(o[dt][4 * q4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d0) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        const int d0 = 32 * dt + 8 * q4 + 4 * hh;
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          const float v = (ws.o[dt][r] * a0 + src[(2 + 16 * dt + r) * 64 + lane] * a1) * inv;
+          b[e] = fpk::f32_to_bf16_bits(v);
+        }
+        *reinterpret_cast<uint2*>(op + d0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
       }
   }
 }
@@ -234,10 +439,9 @@ hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int
   a.nb = dm.nb;
   a.Lpad = dm.nb * dm.B;
   const bool fp8 = p.dtype == FP_FP8_E4M3;
-  a.scale_log2 = sm_scale * (fp8 ? p.q_scale * p.k_scale : 1.0f) * 1.4426950408889634f;
-  a.out_scale = fp8 ? p.v_scale : 1.0f;
-  dim3 grid((unsigned)(dm.nb * dm.Hq));
   if (fp8) return hipErrorInvalidValue;  // e4m3fn inputs take the generic kernel for now
-  hipLaunchKernelGGL(attn_bf16_d128_kernel, grid, dim3(256), 0, st, a);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out_scale = 1.0f;
+  hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3((unsigned)(dm.nb * dm.Hq)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
