@@ -84,7 +84,7 @@ void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {
 }
 
 bool use_mfma(const fp_problem* p, const FpDims& dm) {
-  return p->dtype == FP_BF16 && dm.d == 128 && dm.B == 128;
+  return p->dtype != FP_F32 && dm.d == 128 && dm.B == 128;
 }
 
 int check_ws(const fp_problem* p, const FpDims& dm, void* ws, size_t bytes, fp_ws_layout* w) {

@@ -1,5 +1,12 @@
 // Step 5 on the matrix cores: block-sparse causal attention with GQA over the
-// kept key blocks, bf16 inputs, head_dim 128, block 128.
+// kept key blocks, head_dim 128, block 128, bf16 or e4m3fn inputs.
+//
+// e4m3fn inputs (FlashPrefill V2 abstract: FP8 inference): S^T = K Q^T runs
+// on v_mfma_scale_f32_32x32x64_f8f6f4 straight from the e4m3 codes (unit
+// block scales; the per-tensor scales q_scale*k_scale are folded into the
+// softmax scale), the K tile is staged as 128-byte rows, and P.V stays in
+// bf16: V^T is widened exactly from e4m3 to bf16 by the layout pass and
+// v_scale is applied to the output, so P is not quantised to 8 bits.
 //
 // FlashPrefill skill page, "Architecture Overview" (physical index jumping:
 // only the listed key blocks are visited) and "Implementation Steps" (the
@@ -84,6 +91,51 @@ __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int&
 }
 
 __device__ __forceinline__ int swz(int row) { return (row & 15) ^ (((row >> 3) & 1) << 2); }
+// e4m3 K rows are 128 B (8 chunks): the chunk XOR (row >> 1) & 7 sends the 16
+// rows one operand read touches to 16 different bank groups.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+using fpk::intx8;
+
+// Q fragments (B operand of S^T = K Q^T) for one query row: bf16 holds
+// Q[16s + 8hh .. +7] for 8 steps s; e4m3 holds Q[64s + 32hh .. +31] for 2.
+template <bool kFp8>
+struct QFrag;
+template <>
+struct QFrag<false> {
+  bf16x8 f[8];
+};
+template <>
+struct QFrag<true> {
+  intx8 f[2];
+};
+
+// S^T (32 keys x 32 queries) += K rows `row` of the tile times Q, over the
+// whole head dimension.
+template <bool kFp8>
+__device__ __forceinline__ floatx16 qk_rows(const uint4* sK, const QFrag<kFp8>& q, int row, int hh,
+                                            floatx16 acc) {
+  if constexpr (!kFp8) {
+    const uint4* kr = sK + row * 16;
+    const int x = swz(row) ^ hh;
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&kr[(2 * st) ^ x]),
+                                                    q.f[st], acc, 0, 0, 0);
+  } else {
+    const uint4* kr = sK + row * 8;
+    const int x = swz8(row);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int c0 = 4 * st + 2 * hh;
+      const uint4 lo = kr[c0 ^ x], hi = kr[(c0 + 1) ^ x];
+      const intx8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q.f[st], acc, 0, 0, 0, 127, 0, 127);
+    }
+  }
+  return acc;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -147,35 +199,34 @@ __device__ __forceinline__ void exp_subtile(const floatx16& s, float c, float mu
 // with the exponentials of tile n, then O += P(n) V(n) interleaved with the
 // rest of the exponentials.  sched_group_barrier pins the interleave (MFMA,
 // LDS read, a few VALU) so the in-order wave keeps both pipes busy.
+template <bool kFp8>
 __device__ __forceinline__ void pipelined_step(const uint4* sKn, const uint4* sV,
-                                               const bf16x8* qf, const floatx16* s_cur,
+                                               const QFrag<kFp8>& qf, const floatx16* s_cur,
                                                floatx16* s_nxt, WaveState& ws, float c, int kh,
                                                int qi, int hh, int pm) {
   const float mu = ws.m == -INFINITY ? 0.0f : ws.m;
-  const int row0 = 64 * kh + pm;
-  const int row1 = row0 + 32;
-  const int x0 = swz(row0) ^ hh, x1 = swz(row1) ^ hh;
-  const uint4* k0 = sKn + row0 * 16;
-  const uint4* k1 = sKn + row1 * 16;
-  s_nxt[0] = (floatx16){0};
-  s_nxt[1] = (floatx16){0};
   bf16x8 pb[4];
   float l = ws.l;
-  // -- S(n+1): 16 MFMAs, the two sub-tile chains alternating
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&k0[(2 * st) ^ x0]);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&k1[(2 * st) ^ x1]);
-    s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[st], s_nxt[0], 0, 0, 0);
-    s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[st], s_nxt[1], 0, 0, 0);
-  }
+  // -- S(n+1): the two 32-key sub-tiles of this wave's half
+  s_nxt[0] = qk_rows<kFp8>(sKn, qf, 64 * kh + pm, hh, (floatx16){0});
+  s_nxt[1] = qk_rows<kFp8>(sKn, qf, 64 * kh + 32 + pm, hh, (floatx16){0});
   exp_subtile(s_cur[0], c, mu, l, pb[0], pb[1]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  if constexpr (!kFp8) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    }
   }
   // -- O += P V for this half's 64 keys, with the second sub-tile's exps
   exp_subtile(s_cur[1], c, mu, l, pb[2], pb[3]);
@@ -203,60 +254,68 @@ __device__ __forceinline__ void pipelined_step(const uint4* sKn, const uint4* sV
 }
 
 // S^T sub-tiles of this wave's 64 keys of one K tile (prologue only).
-__device__ __forceinline__ void qk_tile(const uint4* sK, const bf16x8* qf, floatx16* s, int kh,
-                                        int hh, int pm) {
+template <bool kFp8>
+__device__ __forceinline__ void qk_tile(const uint4* sK, const QFrag<kFp8>& qf, floatx16* s,
+                                        int kh, int hh, int pm) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = (floatx16){0};
-    const int row = 64 * kh + 32 * kt + pm;
-    const int sw = swz(row);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sK[row * 16 + ((2 * st + hh) ^ sw)]);
-      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[st], s[kt], 0, 0, 0);
-    }
-  }
+  for (int kt = 0; kt < 2; ++kt) s[kt] = qk_rows<kFp8>(sK, qf, 64 * kh + 32 * kt + pm, hh, (floatx16){0});
 }
 
-// Direct-to-LDS tile loads.  Wave w moves row quads 4w .. 4w+3 of a tile:
-// lane l fills slot l%16 of row 16w + 4e + l/16 with the global chunk
-// (l%16) ^ swz(row).  The per-lane byte offsets are fixed for the whole
-// workgroup; only the uniform tile base moves with the key block.
+// Direct-to-LDS tile loads.  bf16 K and V^T rows are 256 B (16 chunks of
+// 16 B): wave w moves row quads 4w .. 4w+3, lane l filling slot l%16 of row
+// 16w + 4e + l/16 with the global chunk (l%16) ^ swz(row).  e4m3 K rows are
+// 128 B: wave w moves row octets 2w, 2w+1, lane l filling slot l%8 of row
+// 16w + 8e + l/8 with chunk (l%8) ^ swz8(row).  The per-lane byte offsets
+// are fixed for the whole workgroup; only the uniform tile base moves with
+// the key block.
+template <bool kFp8>
 struct TileLoader {
+  static constexpr int kEsz = kFp8 ? 1 : 2;
+  static constexpr int kKLoads = kFp8 ? 2 : 4;  // K loads per wave per tile
   const uint8_t* kbase;  // K of kv head g
   const uint8_t* vbase;  // V^T rows of kv head g
   int64_t k_tile;        // bytes between consecutive key blocks of K
   int64_t k_st;
-  uint32_t koff[4], voff[4];
-  int row[4], chunk[4];
+  uint32_t koff[kKLoads], voff[4];
+  int krow[kKLoads], kchunk[kKLoads];
   int L;
 
   __device__ __forceinline__ void init(const AttnArgs& a, int g, int w, int lane) {
-    kbase = a.k + (int64_t)g * a.k_sh * 2;
+    kbase = a.k + (int64_t)g * a.k_sh * kEsz;
     vbase = reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)g * 128 * a.Lpad * 2;
-    k_tile = (int64_t)128 * a.k_st * 2;
+    k_tile = (int64_t)128 * a.k_st * kEsz;
     k_st = a.k_st;
     L = a.L;
 #pragma unroll
+    for (int e = 0; e < kKLoads; ++e) {
+      if constexpr (!kFp8) {
+        krow[e] = 16 * w + 4 * e + (lane >> 4);
+        kchunk[e] = (lane & 15) ^ swz(krow[e]);
+      } else {
+        krow[e] = 16 * w + 8 * e + (lane >> 3);
+        kchunk[e] = (lane & 7) ^ swz8(krow[e]);
+      }
+      koff[e] = (uint32_t)(krow[e] * a.k_st * kEsz + kchunk[e] * 16);
+    }
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
-      row[e] = 16 * w + 4 * e + (lane >> 4);
-      chunk[e] = (lane & 15) ^ swz(row[e]);
-      koff[e] = (uint32_t)(row[e] * a.k_st * 2 + chunk[e] * 16);
-      voff[e] = (uint32_t)((int64_t)row[e] * a.Lpad * 2 + chunk[e] * 16);
+      const int row = 16 * w + 4 * e + (lane >> 4);
+      voff[e] = (uint32_t)((int64_t)row * a.Lpad * 2 + ((lane & 15) ^ swz(row)) * 16);
     }
   }
   __device__ __forceinline__ void load_k(uint4* sK, int j, int w) const {
     const uint8_t* base = kbase + (int64_t)j * k_tile;
     if (j * 128 + 128 <= L) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        __builtin_amdgcn_global_load_lds(base + koff[e], (lds_ptr_t)(sK + (4 * w + e) * 64), 16, 0, 0);
+      for (int e = 0; e < kKLoads; ++e)
+        __builtin_amdgcn_global_load_lds(base + koff[e], (lds_ptr_t)(sK + (kKLoads * w + e) * 64),
+                                         16, 0, 0);
     } else {  // ragged last block: rows past L repeat row L-1 (masked later)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = min(row[e], L - 1 - j * 128);
-        __builtin_amdgcn_global_load_lds(base + (int64_t)r * k_st * 2 + chunk[e] * 16,
-                                         (lds_ptr_t)(sK + (4 * w + e) * 64), 16, 0, 0);
+      for (int e = 0; e < kKLoads; ++e) {
+        const int r = min(krow[e], L - 1 - j * 128);
+        __builtin_amdgcn_global_load_lds(base + (int64_t)r * k_st * kEsz + kchunk[e] * 16,
+                                         (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16, 0, 0);
       }
     }
   }
@@ -270,7 +329,8 @@ struct TileLoader {
 
 #define FP_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70) /* vmcnt(0) */
 
-__global__ __launch_bounds__(512) void attn_bf16_d128_kernel(AttnArgs a) {
+template <bool kFp8>
+__global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   // K tile m lives in sK[m & 1], V^T tile m in sV[m & 1]; K runs one tile
   // ahead of V because S(n+1) = K(n+1) Q^T is issued before P(n) V(n).
   __shared__ uint4 sK0[kTileU4], sK1[kTileU4];
@@ -306,19 +366,34 @@ __global__ __launch_bounds__(512) void attn_bf16_d128_kernel(AttnArgs a) {
     return __builtin_amdgcn_readlane(win, n - wbase);
   };
 
-  TileLoader ld;
+  TileLoader<kFp8> ld;
   ld.init(a, g, w, lane);
 
-  // B operand of S^T = K Q^T: lane holds Q[tq][16s + 8hh .. +7] for step s.
-  bf16x8 qf[8];
-  if (tq < a.L) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)tq * a.q_st +
-                         (int64_t)h * a.q_sh + 8 * hh;
+  // B operand of S^T = K Q^T for query row tq
+  QFrag<kFp8> qf;
+  if constexpr (!kFp8) {
+    if (tq < a.L) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)tq * a.q_st +
+                           (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+      for (int s = 0; s < 8; ++s) qf.f[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf.f[s] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
   } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < 2; ++s) qf.f[s] = (intx8){0, 0, 0, 0, 0, 0, 0, 0};
+    if (tq < a.L) {
+      const uint8_t* qp = a.q + (int64_t)tq * a.q_st + (int64_t)h * a.q_sh + 32 * hh;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 16);
+        qf.f[s] = (intx8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
   }
 
   // prologue: K(0), K(1), V(0), V(1) in; S(0); then K(2) on its way
@@ -339,7 +414,7 @@ __global__ __launch_bounds__(512) void attn_bf16_d128_kernel(AttnArgs a) {
   FP_WAIT_VMEM();
   __syncthreads();
   floatx16 sA[2], sB[2];
-  qk_tile(sK0, qf, sA, kh, hh, pm);
+  qk_tile<kFp8>(sK0, qf, sA, kh, hh, pm);
   __syncthreads();
   if (cnt > 2) ld.load_k(sK0, j2, w);
 
@@ -349,7 +424,7 @@ __global__ __launch_bounds__(512) void attn_bf16_d128_kernel(AttnArgs a) {
   // Two steps per trip so buffer and register roles are static.
   for (int n = 0; n < cnt; n += 2) {
     softmax_stats(sA, ws, c, j0 == i, qg, kh, qi, hh);
-    pipelined_step(sK1, sV0, qf, sA, sB, ws, c, kh, qi, hh, pm);
+    pipelined_step<kFp8>(sK1, sV0, qf, sA, sB, ws, c, kh, qi, hh, pm);
     FP_WAIT_VMEM();
     __syncthreads();
     {
@@ -362,7 +437,7 @@ __global__ __launch_bounds__(512) void attn_bf16_d128_kernel(AttnArgs a) {
     }
     if (n + 1 >= cnt) break;
     softmax_stats(sB, ws, c, j0 == i, qg, kh, qi, hh);
-    pipelined_step(sK0, sV1, qf, sB, sA, ws, c, kh, qi, hh, pm);
+    pipelined_step<kFp8>(sK0, sV1, qf, sB, sA, ws, c, kh, qi, hh, pm);
     FP_WAIT_VMEM();
     __syncthreads();
     {
@@ -439,9 +514,12 @@ hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int
   a.nb = dm.nb;
   a.Lpad = dm.nb * dm.B;
   const bool fp8 = p.dtype == FP_FP8_E4M3;
-  if (fp8) return hipErrorInvalidValue;  // e4m3fn inputs take the generic kernel for now
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.out_scale = 1.0f;
-  hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3((unsigned)(dm.nb * dm.Hq)), dim3(512), 0, st, a);
+  a.scale_log2 = sm_scale * (fp8 ? p.q_scale * p.k_scale : 1.0f) * 1.4426950408889634f;
+  a.out_scale = fp8 ? p.v_scale : 1.0f;
+  const dim3 grid((unsigned)(dm.nb * dm.Hq));
+  if (fp8)
+    hipLaunchKernelGGL(attn_d128_kernel<true>, grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_d128_kernel<false>, grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
