@@ -43,7 +43,29 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 5 plain device copies of MIB MiB "
+                         "(the known-size kernel that scales the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
+    WRITE_SIZE on these give the counter-to-byte factor."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def kept_pairs(counts, L, B):
@@ -204,6 +226,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     _lib.load_library()
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.config]
@@ -252,7 +277,7 @@ def main():
     flops = 4.0 * d * pairs
     density = float(counts.sum()) / (Hq * nb * (nb + 1) / 2)
     esz = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.dtype]
-    mfma_path = cfg.dtype == "bf16" and d == 128 and B == 128
+    mfma_path = cfg.dtype in ("bf16", "fp8") and d == 128 and B == 128  # V^T pass in pool
     pool_bytes = (L * (Hq + Hkv) * d * esz + (Hq + Hkv) * nb * d * 4
                   + ((L * Hkv * d * esz + Hkv * d * nb * B * 2) if mfma_path else 0))
     sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2

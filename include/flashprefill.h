@@ -97,7 +97,9 @@ typedef struct fp_problem {
  *   indices int32, triangular: row (h,i) starts at h*nb*(nb+1)/2 + i*(i+1)/2, holds
  *           counts[h][i] ascending key-block indices (capacity i+1)
  *   v_t     bf16 [num_kv_heads][head_dim][nb*block_size]  V transposed per kv head, zero past
- *           seq_len (written by fp_block_pool; zero-length for fp32 inputs)
+ *           seq_len; e4m3 codes are widened to bf16 exactly, v_scale is applied at the output
+ *           (written by fp_block_pool; zero-length unless the input is bf16 or e4m3 with
+ *           head_dim 128 and block_size 128)
  * The layout is part of the ABI: a caller may read the selection, or write
  * its own counts/indices (ascending, each list ending with its diagonal
  * block i) before fp_sparse_prefill to run attention on a given mask. */
@@ -110,8 +112,8 @@ typedef struct fp_ws_layout {
 int fp_workspace_layout(const fp_problem* p, fp_ws_layout* layout);
 
 /* Step 1.  Reads q and k and writes the q_pool and k_pool sections.  For
- * bf16 inputs with head_dim 128 and block_size 128 it also reads v and writes
- * the v_t section (the key-contiguous V layout the matrix-core attention
+ * bf16 or e4m3 inputs with head_dim 128 and block_size 128 it also reads v and
+ * writes the v_t section (the key-contiguous V layout the matrix-core attention
  * reads), so that stage streams V once here rather than inside the attention
  * loop. */
 int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
