@@ -24,23 +24,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// OCP e4m3fn code -> fp32 (exact).  bias 7; exponent 0 is subnormal
-// (m * 2^-9); S.1111.111 is NaN; there are no infinities.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 24;
-  uint32_t e = (c >> 3) & 0xfu;
-  uint32_t m = c & 0x7u;
-  if (e == 0) {
-    float v = (float)m * 0.001953125f;  // 2^-9
-    return s ? -v : v;
-  }
-  if (e == 15 && m == 7) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+// OCP e4m3fn codes -> fp32 (exact: bias 7, exponent 0 subnormal, S.1111.111
+// NaN, no infinities).  On gfx950 the fp8 conversion instructions read the
+// OCP format; one v_cvt_pk_f32_fp8 widens the two codes of a 16-bit half.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
 }
 
-// e4m3fn code -> bf16 bits (exact: every e4m3 value is a bf16 value)
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  return __float_as_uint(e4m3_to_f32(c)) >> 16;
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)(c & 0xffu), 0);
 }
 
 __host__ __device__ __forceinline__ int64_t tri_offset(int64_t h, int64_t i, int64_t nb) {

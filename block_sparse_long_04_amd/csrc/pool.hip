@@ -38,8 +38,10 @@ __device__ __forceinline__ void accum(float* acc, const uint4& v) {
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      float f[4];
+      fpk::e4m3x4_to_f32(w[e], f);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[4 * e + b] += fpk::e4m3_to_f32((w[e] >> (8 * b)) & 0xffu);
+      for (int b = 0; b < 4; ++b) acc[4 * e + b] += f[b];
     }
   }
 }

@@ -37,9 +37,10 @@ __global__ __launch_bounds__(256) void vtrans_kernel(const uint8_t* __restrict__
         tile[tr][cc * VEC + 2 * e] = (uint16_t)(w[e] & 0xffffu);
         tile[tr][cc * VEC + 2 * e + 1] = (uint16_t)(w[e] >> 16);
       } else {
+        float f[4];
+        fpk::e4m3x4_to_f32(w[e], f);  // every e4m3 value is a bf16 value: truncation is exact
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          tile[tr][cc * VEC + 4 * e + b] = (uint16_t)fpk::e4m3_to_bf16_bits((w[e] >> (8 * b)) & 0xffu);
+        for (int b = 0; b < 4; ++b) tile[tr][cc * VEC + 4 * e + b] = (uint16_t)(__float_as_uint(f[b]) >> 16);
       }
     }
   }

@@ -149,3 +149,40 @@ def test_c2_full_layer_parity():
     assert bad == 0
     want = O.sparse_attention(ref["q"], ref["k"], ref["v"], res["lists"], 128, sm_scale(layer))
     check_out(res["out"], want, "bf16")
+
+
+def test_e4m3_decode_of_every_code_in_pool_and_vt():
+    """Every e4m3fn code (NaN included) reaches the pooled proxies and the
+    V^T layout with exactly the value torch's own e4m3fn decode gives.  With
+    L = 129 and B = 128, token 128 is a one-token last block, whose mean is
+    the token itself."""
+    dev = require_gpu()
+    say("[e4m3 decode] all 256 codes")
+    L, H, d, B = 129, 2, 128, 128
+    g = torch.Generator(device="cpu").manual_seed(7)
+    codes = torch.randint(0, 256, (L, H, d), generator=g, dtype=torch.int32)
+    codes[codes == 0x7f] = 0x10
+    codes[codes == 0xff] = 0x90
+    codes[128] = torch.arange(256, dtype=torch.int32).view(H, d)  # the lone token of block 1
+    q8 = codes.to(torch.uint8).view(torch.float8_e4m3fn)
+    k8 = q8.clone()
+    v8 = q8.clone()
+    q, k, v = q8.to(dev), k8.to(dev), v8.to(dev)
+    pf = _lib.Prefill(q, k, v, block_size=B, threshold=0.1, q_scale=1.0, k_scale=1.0, v_scale=1.0)
+    pf.pool()
+    torch.cuda.synchronize()
+    want = q8[128].float()  # torch decode, [H, d]
+    for got in (pf.ws.k_pool()[:, 1, :].cpu(), pf.ws.q_pool()[:, 1, :].cpu()):
+        assert torch.equal(torch.isnan(got), torch.isnan(want))
+        fin = ~torch.isnan(want)
+        assert torch.equal(got[fin], want[fin])
+    # V^T: [Hkv][d][nb*B] bf16, token 128 of every (kv head, dim) row
+    lay = pf.ws.layout
+    nb = 2
+    vt = pf.ws.buf[lay.v_t: lay.v_t + H * d * nb * B * 2].view(torch.bfloat16).view(H, d, nb * B)
+    col = vt[:, :, 128].float().cpu()
+    assert torch.equal(torch.isnan(col), torch.isnan(want))
+    fin = ~torch.isnan(want)
+    assert torch.equal(col[fin], want[fin])
+    # zero padding past L
+    assert torch.count_nonzero(vt[:, :, L:].float()).item() == 0
