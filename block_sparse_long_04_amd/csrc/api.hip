@@ -64,6 +64,16 @@ int check_problem(const fp_problem* p, FpDims* dm) {
   return FP_OK;
 }
 
+// The matrix-core attention serves bf16 and e4m3 inputs with d = B = 128.
+// It addresses one kv head of K through 32-bit buffer offsets, so every key
+// row of the padded sequence must start below 2^31 bytes from the head's
+// base; larger token strides go to the generic kernel.
+bool use_mfma(const fp_problem* p, const FpDims& dm) {
+  if (p->dtype == FP_F32 || dm.d != 128 || dm.B != 128) return false;
+  const int64_t esz = p->dtype == FP_BF16 ? 2 : 1;
+  return (int64_t)dm.nb * dm.B * p->k_stride_tok * esz + dm.d * esz < (int64_t(1) << 31);
+}
+
 void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {
   const size_t nb = (size_t)dm.nb;
   size_t off = 0;
@@ -78,14 +88,10 @@ void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {
   w->indices = off;
   off = align_up(off + (size_t)dm.Hq * (nb * (nb + 1) / 2) * sizeof(int));
   w->v_t = off;
-  const bool mfma = p->dtype != FP_F32 && dm.d == 128 && dm.B == 128;
-  if (mfma) off = align_up(off + (size_t)dm.Hkv * dm.d * nb * dm.B * sizeof(uint16_t));
+  if (use_mfma(p, dm)) off = align_up(off + (size_t)dm.Hkv * dm.d * nb * dm.B * sizeof(uint16_t));
   w->total = off;
 }
 
-bool use_mfma(const fp_problem* p, const FpDims& dm) {
-  return p->dtype != FP_F32 && dm.d == 128 && dm.B == 128;
-}
 
 int check_ws(const fp_problem* p, const FpDims& dm, void* ws, size_t bytes, fp_ws_layout* w) {
   layout_of(p, dm, w);

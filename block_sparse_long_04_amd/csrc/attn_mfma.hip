@@ -145,26 +145,40 @@ struct WaveState {
   float l;  // this lane's partial row sum
 };
 
-// Softmax statistics of one tile's logits: causal mask on the diagonal block,
-// row max, and the lazy raise of the running max (rescaling O and l).
-__device__ __forceinline__ void softmax_stats(floatx16* s, WaveState& ws, float c, bool diag,
-                                              int qg, int kh, int qi, int hh) {
-  if (diag) {
-    const int qrel = 32 * qg + qi;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int krel = 64 * kh + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
-        if (krel > qrel) s[kt][r] = -INFINITY;
-      }
-  }
-  float mx = -INFINITY;
+// Lanes l and l ^ 32 hold the two 16-key halves of one query's logits:
+// v_permlane32_swap exchanges the half-waves without an LDS round trip.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Causal mask of the diagonal block: key 64kh + 32kt + 16(r/8) + 8hh + r%8
+// of this wave's half is dropped for query 32qg + qi when it lies later.
+__device__ __forceinline__ void mask_diag(floatx16* s, int qg, int kh, int qi, int hh) {
+  const int qrel = 32 * qg + qi;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 0; r < 16; ++r) {
+      const int krel = 64 * kh + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
+      if (krel > qrel) s[kt][r] = -INFINITY;
+    }
+}
+
+__device__ __forceinline__ float tile_max(const floatx16* s) {
+  float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    a = fmaxf(a, fmaxf(s[0][r], s[0][r + 1]));
+    b = fmaxf(b, fmaxf(s[1][r], s[1][r + 1]));
+  }
+  return fmaxf(a, b);
+}
+
+// Lazy raise of the running max: only when some query's tile max (mx, both
+// half-waves combined, raw logits) exceeds it by more than kLazy in log2
+// units are O and l rescaled.
+__device__ __forceinline__ void raise_max(WaveState& ws, float mx, float c) {
   const float mxs = mx * c;
   if (__any(mxs > ws.m + kLazy)) {
     const float m_new = fmaxf(ws.m, mxs);
@@ -176,81 +190,157 @@ __device__ __forceinline__ void softmax_stats(floatx16* s, WaveState& ws, float 
   }
 }
 
-// exp2 of one 32-key sub-tile into bf16 P (two 8-key runs); the row sum is
-// taken from the bf16 values themselves with v_dot2 against (1, 1), so l
-// normalises exactly the weights that enter P.V.
-__device__ __forceinline__ void exp_subtile(const floatx16& s, float c, float mu, float& l,
-                                            bf16x8& p0, bf16x8& p1) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(s[r] * c - mu);
-    if (r < 8) p0[r] = p;
-    else p1[r - 8] = p;
-  }
+// exp2 of one logit (scaled to log2 units, shifted by the running max).
+__device__ __forceinline__ float exp_one(float v, float c, float mu) {
+  return __builtin_amdgcn_exp2f(v * c - mu);
+}
+
+// One bf16 pair of P from two exponentials; the row sum takes the bf16
+// values themselves (v_dot2 against (1, 1)), so l normalises exactly the
+// weights that enter P.V.
+__device__ __forceinline__ uint32_t pack_pair(float e0, float e1, float& l) {
+  const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  l = __builtin_amdgcn_fdot2_f32_bf16(pp, one, l, false);
+  return __builtin_bit_cast(uint32_t, pp);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t* w) {
+  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// max(a, b, c) in one v_max3_f32.  (fmaxf on matrix-core results costs an
+// extra canonicalising max per operand.)  Used only on logits written by
+// products issued at least eight matrix-core slots earlier, far beyond the
+// matrix-to-vector read hazard distance.
+__device__ __forceinline__ float max3_late(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Per-step softmax context of one wave.
+struct StepCtx {
+  float c, mu, l;
+  uint32_t pw[4][4];  // P(n) in bf16 pairs: pw[u] is the B operand of PV slots 4u .. 4u+3
+  float e_hold[2];    // first exponential of a pair whose partner comes a slot later
+};
+
+// Phase 1 of step n, in issue order: S(n+1) = K(n+1) Q^T, the two 32-key
+// sub-tiles as alternating accumulation chains.  Every slot holds one MFMA
+// whose LDS operand was read three slots earlier (a ring of four fragments);
+// sched_barrier fences keep the slots in this order, so each LDS wait is for
+// the oldest read only.  The VALU gaps carry exponentials of P(n): bf16 does
+// all of sub-tile 0 and the first half of sub-tile 1 (1.5 per slot); e4m3,
+// whose four products are twice as long, does sub-tile 0 (4 per slot).
+template <bool kFp8>
+__device__ __forceinline__ void phase1(const uint4* sKn, const QFrag<kFp8>& qf, const floatx16* s_cur,
+                                       floatx16* s_nxt, StepCtx& x, int kh, int hh, int pm) {
+  s_nxt[0] = (floatx16){0};
+  s_nxt[1] = (floatx16){0};
+  const int r0 = 64 * kh + pm;  // sub-tile 1 is rows r0 + 32, same swizzle
+  if constexpr (!kFp8) {
+    const uint4* k0 = sKn + r0 * 16;
+    const int xs = swz(r0) ^ hh;
+    auto kread = [&](int m) -> bf16x8 {  // slot m: sub-tile m & 1, head-dim step m >> 1
+      return *reinterpret_cast<const bf16x8*>(&k0[(m & 1) * 512 + ((2 * (m >> 1)) ^ xs)]);
+    };
+    bf16x8 ka[4];
+    ka[0] = kread(0);
+    ka[1] = kread(1);
+    ka[2] = kread(2);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    l = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p0[2 * e], p0[2 * e + 1]}, one, l, false);
-    l = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){p1[2 * e], p1[2 * e + 1]}, one, l, false);
+    for (int m = 0; m < 16; ++m) {
+      if (m + 3 < 16) ka[(m + 3) & 3] = kread(m + 3);
+      s_nxt[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[m & 3], qf.f[m >> 1], s_nxt[m & 1], 0, 0, 0);
+      const float e = exp_one(s_cur[0][m], x.c, x.mu);
+      if (m & 1) x.pw[m >> 3][(m & 7) >> 1] = pack_pair(x.e_hold[0], e, x.l);
+      else x.e_hold[0] = e;
+      if (!(m & 1)) {
+        const int v = m >> 1;  // sub-tile 1, values 0 .. 7
+        const float e1 = exp_one(s_cur[1][v], x.c, x.mu);
+        if (v & 1) x.pw[2][v >> 1] = pack_pair(x.e_hold[1], e1, x.l);
+        else x.e_hold[1] = e1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    const uint4* k0 = sKn + r0 * 8;
+    const int xs = swz8(r0);
+    auto kread = [&](int m, int part) -> uint4 {  // slot m: sub-tile m & 1, 64-dim step m >> 1
+      return k0[(m & 1) * 256 + ((4 * (m >> 1) + 2 * hh + part) ^ xs)];
+    };
+    uint4 ka[3][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      ka[m][0] = kread(m, 0);
+      ka[m][1] = kread(m, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m + 2 < 4) {
+        ka[(m + 2) % 3][0] = kread(m + 2, 0);
+        ka[(m + 2) % 3][1] = kread(m + 2, 1);
+      }
+      const uint4 lo = ka[m % 3][0], hi = ka[m % 3][1];
+      const intx8 f = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      s_nxt[m & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, qf.f[m >> 1], s_nxt[m & 1], 0, 0,
+                                                                     0, 127, 0, 127);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int v = 4 * m + 2 * e;
+        x.pw[v >> 3][(v & 7) >> 1] =
+            pack_pair(exp_one(s_cur[0][v], x.c, x.mu), exp_one(s_cur[0][v + 1], x.c, x.mu), x.l);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
-// One pipelined step: S(n+1) = K(n+1) Q^T on the matrix cores interleaved
-// with the exponentials of tile n, then O += P(n) V(n) interleaved with the
-// rest of the exponentials.  sched_group_barrier pins the interleave (MFMA,
-// LDS read, a few VALU) so the in-order wave keeps both pipes busy.
+// Phase 2 of step n: O += P(n) V(n), slot m = key group u = m >> 2 times
+// head dims 32 (m & 3) .. +31.  V^T row 32 dt + qi has the same swizzle for
+// every dt, so one address per u serves a group.  Slots 0-7 finish P(n)'s
+// exponentials (bf16: sub-tile 1 values 8-15, ready before slot 12 reads
+// them; e4m3: all of sub-tile 1, two per slot), slots 8-15 take the row max
+// of S(n+1) for the next step.  Returns that max (this lane's half).
 template <bool kFp8>
-__device__ __forceinline__ void pipelined_step(const uint4* sKn, const uint4* sV,
-                                               const QFrag<kFp8>& qf, const floatx16* s_cur,
-                                               floatx16* s_nxt, WaveState& ws, float c, int kh,
-                                               int qi, int hh, int pm) {
-  const float mu = ws.m == -INFINITY ? 0.0f : ws.m;
-  bf16x8 pb[4];
-  float l = ws.l;
-  // -- S(n+1): the two 32-key sub-tiles of this wave's half
-  s_nxt[0] = qk_rows<kFp8>(sKn, qf, 64 * kh + pm, hh, (floatx16){0});
-  s_nxt[1] = qk_rows<kFp8>(sKn, qf, 64 * kh + 32 + pm, hh, (floatx16){0});
-  exp_subtile(s_cur[0], c, mu, l, pb[0], pb[1]);
-  if constexpr (!kFp8) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+__device__ __forceinline__ float phase2(const uint4* sV, const floatx16* s_cur, const floatx16* s_nxt,
+                                        WaveState& ws, StepCtx& x, int kh, int qi, int hh) {
+  const int xv = (8 * kh) ^ hh ^ swz(qi);
+  const uint4* vr = sV + qi * 16;
+  auto vread = [&](int m) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(&vr[(m & 3) * 512 + ((2 * (m >> 2)) ^ xv)]);
+  };
+  bf16x8 va[4];
+  va[0] = vread(0);
+  va[1] = vread(1);
+  va[2] = vread(2);
+  float mx0 = -INFINITY, mx1 = -INFINITY;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  for (int m = 0; m < 16; ++m) {
+    if (m + 3 < 16) va[(m + 3) & 3] = vread(m + 3);
+    ws.o[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m & 3], as_bf16x8(x.pw[m >> 2]), ws.o[m & 3], 0, 0, 0);
+    if (m < 8) {
+      if constexpr (!kFp8) {
+        const float e = exp_one(s_cur[1][8 + m], x.c, x.mu);
+        if (m & 1) x.pw[3][m >> 1] = pack_pair(x.e_hold[1], e, x.l);
+        else x.e_hold[1] = e;
+      } else {
+        x.pw[2 + (m >> 2)][m & 3] =
+            pack_pair(exp_one(s_cur[1][2 * m], x.c, x.mu), exp_one(s_cur[1][2 * m + 1], x.c, x.mu), x.l);
+      }
+    } else {
+      const int r = 2 * (m - 8);
+      mx0 = max3_late(mx0, s_nxt[0][r], s_nxt[0][r + 1]);
+      mx1 = max3_late(mx1, s_nxt[1][r], s_nxt[1][r + 1]);
     }
-  } else {
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // -- O += P V for this half's 64 keys, with the second sub-tile's exps
-  exp_subtile(s_cur[1], c, mu, l, pb[2], pb[3]);
-  const int xv = (8 * kh) ^ hh;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int drow = 32 * dt + qi;
-      const bf16x8 av =
-          *reinterpret_cast<const bf16x8*>(&sV[drow * 16 + ((2 * u) ^ xv ^ swz(drow))]);
-      ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[u], ws.o[dt], 0, 0, 0);
-    }
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-  ws.l = l;
+  return fmaxf(mx0, mx1);
 }
 
 // S^T sub-tiles of this wave's 64 keys of one K tile (prologue only).
@@ -265,27 +355,36 @@ __device__ __forceinline__ void qk_tile(const uint4* sK, const QFrag<kFp8>& qf, 
 // 16 B): wave w moves row quads 4w .. 4w+3, lane l filling slot l%16 of row
 // 16w + 4e + l/16 with the global chunk (l%16) ^ swz(row).  e4m3 K rows are
 // 128 B: wave w moves row octets 2w, 2w+1, lane l filling slot l%8 of row
-// 16w + 8e + l/8 with chunk (l%8) ^ swz8(row).  The per-lane byte offsets
-// are fixed for the whole workgroup; only the uniform tile base moves with
-// the key block.
+// 16w + 8e + l/8 with chunk (l%8) ^ swz8(row).
+//
+// The loads are buffer_load ... lds through a buffer resource per kv head:
+// the per-lane byte offsets are fixed for the whole workgroup and the key
+// block only moves the scalar offset, so a tile costs no vector address
+// arithmetic.  (Buffer loads also keep LDS-read waits exact: while a flat or
+// global LDS load is in flight the compiler can only wait for every LDS
+// read, which would serialise the operand prefetch of the matrix products.)
+// The host guarantees every offset of a kv head fits in 31 bits.
 template <bool kFp8>
 struct TileLoader {
   static constexpr int kEsz = kFp8 ? 1 : 2;
   static constexpr int kKLoads = kFp8 ? 2 : 4;  // K loads per wave per tile
-  const uint8_t* kbase;  // K of kv head g
-  const uint8_t* vbase;  // V^T rows of kv head g
-  int64_t k_tile;        // bytes between consecutive key blocks of K
-  int64_t k_st;
+  __amdgpu_buffer_rsrc_t krs;  // K of kv head g
+  __amdgpu_buffer_rsrc_t vrs;  // V^T rows of kv head g
+  int k_tile;                  // bytes between consecutive key blocks of K
+  int k_row;                   // bytes between consecutive keys
   uint32_t koff[kKLoads], voff[4];
   int krow[kKLoads], kchunk[kKLoads];
   int L;
 
   __device__ __forceinline__ void init(const AttnArgs& a, int g, int w, int lane) {
-    kbase = a.k + (int64_t)g * a.k_sh * kEsz;
-    vbase = reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)g * 128 * a.Lpad * 2;
-    k_tile = (int64_t)128 * a.k_st * kEsz;
-    k_st = a.k_st;
+    k_row = (int)(a.k_st * kEsz);
+    k_tile = 128 * k_row;
     L = a.L;
+    const int k_extent = (a.L - 1) * k_row + 128 * kEsz;
+    krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k + (int64_t)g * a.k_sh * kEsz), 0,
+                                            k_extent, 0x00020000);
+    vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.vt + (int64_t)g * 128 * a.Lpad), 0, 128 * a.Lpad * 2, 0x00020000);
 #pragma unroll
     for (int e = 0; e < kKLoads; ++e) {
       if constexpr (!kFp8) {
@@ -295,46 +394,67 @@ struct TileLoader {
         krow[e] = 16 * w + 8 * e + (lane >> 3);
         kchunk[e] = (lane & 7) ^ swz8(krow[e]);
       }
-      koff[e] = (uint32_t)(krow[e] * a.k_st * kEsz + kchunk[e] * 16);
+      koff[e] = (uint32_t)(krow[e] * k_row + kchunk[e] * 16);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * w + 4 * e + (lane >> 4);
-      voff[e] = (uint32_t)((int64_t)row * a.Lpad * 2 + ((lane & 15) ^ swz(row)) * 16);
+      voff[e] = (uint32_t)(row * a.Lpad * 2 + ((lane & 15) ^ swz(row)) * 16);
     }
   }
   __device__ __forceinline__ void load_k(uint4* sK, int j, int w) const {
-    const uint8_t* base = kbase + (int64_t)j * k_tile;
+    const int soff = j * k_tile;
     if (j * 128 + 128 <= L) {
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e)
-        __builtin_amdgcn_global_load_lds(base + koff[e], (lds_ptr_t)(sK + (kKLoads * w + e) * 64),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
+                                                 koff[e], soff, 0, 0);
     } else {  // ragged last block: rows past L repeat row L-1 (masked later)
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e) {
         const int r = min(krow[e], L - 1 - j * 128);
-        __builtin_amdgcn_global_load_lds(base + (int64_t)r * k_st * kEsz + kchunk[e] * 16,
-                                         (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
+                                                 (uint32_t)(r * k_row + kchunk[e] * 16), soff, 0, 0);
       }
     }
   }
   __device__ __forceinline__ void load_v(uint4* sV, int j, int w) const {
-    const uint8_t* base = vbase + (int64_t)j * 256;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      __builtin_amdgcn_global_load_lds(base + voff[e], (lds_ptr_t)(sV + (4 * w + e) * 64), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(sV + (4 * w + e) * 64), 16, voff[e],
+                                               j * 256, 0, 0);
   }
 };
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
+// | vmcnt[15:14]): wait for vector memory only, leaving N loads in flight.
 #define FP_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70) /* vmcnt(0) */
+
+// Workgroup barrier of the tile pipeline.  Each wave first waits until at
+// most n of its own LDS-bound loads are in flight (the older group has
+// landed) and all its LDS reads have returned; the barrier then makes the
+// landed tile visible to every wave and lets the freed buffer be refilled.
+// (__syncthreads would also drain the younger loads: its release fence waits
+// for all outstanding vector memory.)  The empty asm statements keep the
+// compiler from moving LDS accesses across the barrier.
+template <int n>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14)); /* vmcnt(n) lgkmcnt(0) */
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <bool kFp8>
 __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   // K tile m lives in sK[m & 1], V^T tile m in sV[m & 1]; K runs one tile
   // ahead of V because S(n+1) = K(n+1) Q^T is issued before P(n) V(n).
-  __shared__ uint4 sK0[kTileU4], sK1[kTileU4];
-  __shared__ uint4 sV0[kTileU4], sV1[kTileU4];
+  __shared__ uint4 smem[4 * kTileU4];
+  uint4* const sK0 = smem;
+  uint4* const sK1 = smem + kTileU4;
+  uint4* const sV0 = smem + 2 * kTileU4;
+  uint4* const sV1 = smem + 3 * kTileU4;
 
   int h, i;
   work_item(blockIdx.x, a.nb, a.Hq, a.Hkv, h, i);
@@ -359,9 +479,10 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   int win = lst[min(lane, cnt - 1)];
   int wbase = 0;
   auto entry = [&](int n) -> int {
-    if (n - wbase >= 64) {
+    if (n - wbase >= 64) {  // rare: wait right here, so no wait sits on the common path
       wbase += 64;
       win = lst[min(wbase + lane, cnt - 1)];
+      FP_WAIT_VMEM();
     }
     return __builtin_amdgcn_readlane(win, n - wbase);
   };
@@ -396,16 +517,21 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
     }
   }
 
-  // prologue: K(0), K(1), V(0), V(1) in; S(0); then K(2) on its way
+  // Load schedule.  Buffers: K(m) in sK[m & 1], V(m) in sV[m & 1].  Step n
+  // computes S(n+1) from K(n+1) (phase 1) and O += P(n) V(n) (phase 2):
+  //   after phase 1, a barrier frees K(n+1)'s buffer and K(n+3) is issued;
+  //   after phase 2, a barrier frees V(n)'s buffer and V(n+2) is issued.
+  // Each load thus has one and a half steps to land.  Loads go out in the
+  // order ... K(n+2), V(n+1), K(n+3), V(n+2) ..., so before each barrier
+  // the wait leaves the two younger groups in flight (vmcnt(kK + kV)); near
+  // the end of the list, where fewer groups are in flight, it waits for all.
+  constexpr int kK = TileLoader<kFp8>::kKLoads;
   int j0 = entry(0);
   int j1 = cnt > 1 ? entry(1) : 0;
   int j2 = cnt > 2 ? entry(2) : 0;
   ld.load_k(sK0, j0, w);
   ld.load_v(sV0, j0, w);
-  if (cnt > 1) {
-    ld.load_k(sK1, j1, w);
-    ld.load_v(sV1, j1, w);
-  }
+  if (cnt > 1) ld.load_k(sK1, j1, w);
   WaveState ws;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) ws.o[dt] = (floatx16){0};
@@ -416,37 +542,49 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   floatx16 sA[2], sB[2];
   qk_tile<kFp8>(sK0, qf, sA, kh, hh, pm);
   __syncthreads();
-  if (cnt > 2) ld.load_k(sK0, j2, w);
+  if (cnt > 2) ld.load_k(sK0, j2, w);  // issued as step -1's phase-1 load
+  if (cnt > 1) ld.load_v(sV1, j1, w);  // and as its phase-2 load
+  if (j0 == i) mask_diag(sA, qg, kh, qi, hh);
+  float mx = pair_max(tile_max(sA));
 
-  // Step n (tiles n and n+1 live in the S registers and K buffers):
-  //   mask/max/rescale of S(n); S(n+1) || exp(S(n)); O += P(n) V(n);
-  //   wait + barrier; prefetch K(n+3) into K(n+1)'s buffer, V(n+2) into V(n)'s.
+  StepCtx x;
+  x.c = c;
+  int jn3 = 0;
   // Two steps per trip so buffer and register roles are static.
   for (int n = 0; n < cnt; n += 2) {
-    softmax_stats(sA, ws, c, j0 == i, qg, kh, qi, hh);
-    pipelined_step<kFp8>(sK1, sV0, qf, sA, sB, ws, c, kh, qi, hh, pm);
-    FP_WAIT_VMEM();
-    __syncthreads();
-    {
-      const int j3 = n + 3 < cnt ? entry(n + 3) : 0;
-      if (n + 3 < cnt) ld.load_k(sK1, j3, w);
-      if (n + 2 < cnt) ld.load_v(sV0, j2, w);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int t = n + half;  // this step
+      if (half == 1 && t >= cnt) break;
+      floatx16* s_cur = half == 0 ? sA : sB;
+      floatx16* s_nxt = half == 0 ? sB : sA;
+      uint4* sKn = half == 0 ? sK1 : sK0;
+      uint4* sVc = half == 0 ? sV0 : sV1;
+      raise_max(ws, mx, c);
+      x.mu = ws.m == -INFINITY ? 0.0f : ws.m;
+      x.l = ws.l;
+      phase1<kFp8>(sKn, qf, s_cur, s_nxt, x, kh, hh, pm);
+      // V(t) must have landed; K(t+2) and V(t+1) may still be in flight
+      if (t + 2 < cnt) tile_barrier<kK + 4>();
+      else tile_barrier<0>();
+      if (t + 3 < cnt) {
+        jn3 = entry(t + 3);
+        ld.load_k(sKn, jn3, w);
+      }
+      mx = phase2<kFp8>(sVc, s_cur, s_nxt, ws, x, kh, qi, hh);
+      ws.l = x.l;
+      if (t + 1 < cnt && j1 == i) {
+        mask_diag(s_nxt, qg, kh, qi, hh);
+        mx = tile_max(s_nxt);
+      }
+      mx = pair_max(mx);
+      // K(t+2) must have landed; V(t+1) and K(t+3) may still be in flight
+      if (t + 3 < cnt) tile_barrier<kK + 4>();
+      else tile_barrier<0>();
+      if (t + 2 < cnt) ld.load_v(sVc, j2, w);
       j0 = j1;
       j1 = j2;
-      j2 = j3;
-    }
-    if (n + 1 >= cnt) break;
-    softmax_stats(sB, ws, c, j0 == i, qg, kh, qi, hh);
-    pipelined_step<kFp8>(sK0, sV1, qf, sB, sA, ws, c, kh, qi, hh, pm);
-    FP_WAIT_VMEM();
-    __syncthreads();
-    {
-      const int j3 = n + 4 < cnt ? entry(n + 4) : 0;
-      if (n + 4 < cnt) ld.load_k(sK0, j3, w);
-      if (n + 3 < cnt) ld.load_v(sV1, j2, w);
-      j0 = j1;
-      j1 = j2;
-      j2 = j3;
+      j2 = jn3;
     }
   }
 
