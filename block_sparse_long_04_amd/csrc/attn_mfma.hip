@@ -65,6 +65,9 @@ struct AttnArgs {
 };
 
 constexpr int kTileU4 = 128 * 16;  // one 128 x 256 B tile in uint4
+constexpr int kMergeBytes = 4 * 66 * 64 * 4;  // key-half merge area: [qg][m, l, 64 O rows][64 lanes] floats
+constexpr int kStageRow = 272;                 // staged bf16 output row (256 B + 16 B pad)
+static_assert(kMergeBytes % 16 == 0 && kMergeBytes + 4 * 32 * kStageRow <= 4 * kTileU4 * 16, "LDS epilogue fits");
 constexpr float kLazy = 8.0f;      // lazy-max slack in log2 units
 
 __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int& h, int& i) {
@@ -205,6 +208,16 @@ __device__ __forceinline__ uint32_t pack_pair(float e0, float e1, float& l) {
   return __builtin_bit_cast(uint32_t, pp);
 }
 
+// Pins a value to this point of the instruction stream.  P(n) computed in
+// phase 1 is only used by phase 2's products, after a barrier and a branch;
+// without the pin the optimiser sinks those exponentials into phase 2's
+// block, where they run as one long VALU stretch instead of in the gaps of
+// phase 1's matrix products.
+__device__ __forceinline__ uint32_t pin(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t* w) {
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
@@ -255,12 +268,12 @@ __device__ __forceinline__ void phase1(const uint4* sKn, const QFrag<kFp8>& qf, 
       if (m + 3 < 16) ka[(m + 3) & 3] = kread(m + 3);
       s_nxt[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[m & 3], qf.f[m >> 1], s_nxt[m & 1], 0, 0, 0);
       const float e = exp_one(s_cur[0][m], x.c, x.mu);
-      if (m & 1) x.pw[m >> 3][(m & 7) >> 1] = pack_pair(x.e_hold[0], e, x.l);
+      if (m & 1) x.pw[m >> 3][(m & 7) >> 1] = pin(pack_pair(x.e_hold[0], e, x.l));
       else x.e_hold[0] = e;
       if (!(m & 1)) {
         const int v = m >> 1;  // sub-tile 1, values 0 .. 7
         const float e1 = exp_one(s_cur[1][v], x.c, x.mu);
-        if (v & 1) x.pw[2][v >> 1] = pack_pair(x.e_hold[1], e1, x.l);
+        if (v & 1) x.pw[2][v >> 1] = pin(pack_pair(x.e_hold[1], e1, x.l));
         else x.e_hold[1] = e1;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -293,7 +306,7 @@ __device__ __forceinline__ void phase1(const uint4* sKn, const QFrag<kFp8>& qf, 
       for (int e = 0; e < 2; ++e) {
         const int v = 4 * m + 2 * e;
         x.pw[v >> 3][(v & 7) >> 1] =
-            pack_pair(exp_one(s_cur[0][v], x.c, x.mu), exp_one(s_cur[0][v + 1], x.c, x.mu), x.l);
+            pin(pack_pair(exp_one(s_cur[0][v], x.c, x.mu), exp_one(s_cur[0][v + 1], x.c, x.mu), x.l));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -373,8 +386,15 @@ struct TileLoader {
   int k_tile;                  // bytes between consecutive key blocks of K
   int k_row;                   // bytes between consecutive keys
   uint32_t koff[kKLoads], voff[4];
-  int krow[kKLoads], kchunk[kKLoads];
   int L;
+
+  // key row and 16-byte chunk that load e of wave w, lane `lane` moves
+  __device__ __forceinline__ static int krow_of(int w, int e, int lane) {
+    return kFp8 ? 16 * w + 8 * e + (lane >> 3) : 16 * w + 4 * e + (lane >> 4);
+  }
+  __device__ __forceinline__ static int kchunk_of(int row, int lane) {
+    return kFp8 ? (lane & 7) ^ swz8(row) : (lane & 15) ^ swz(row);
+  }
 
   __device__ __forceinline__ void init(const AttnArgs& a, int g, int w, int lane) {
     k_row = (int)(a.k_st * kEsz);
@@ -387,14 +407,8 @@ struct TileLoader {
         const_cast<uint16_t*>(a.vt + (int64_t)g * 128 * a.Lpad), 0, 128 * a.Lpad * 2, 0x00020000);
 #pragma unroll
     for (int e = 0; e < kKLoads; ++e) {
-      if constexpr (!kFp8) {
-        krow[e] = 16 * w + 4 * e + (lane >> 4);
-        kchunk[e] = (lane & 15) ^ swz(krow[e]);
-      } else {
-        krow[e] = 16 * w + 8 * e + (lane >> 3);
-        kchunk[e] = (lane & 7) ^ swz8(krow[e]);
-      }
-      koff[e] = (uint32_t)(krow[e] * k_row + kchunk[e] * 16);
+      const int row = krow_of(w, e, lane);
+      koff[e] = (uint32_t)(row * k_row + kchunk_of(row, lane) * 16);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -410,11 +424,13 @@ struct TileLoader {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
                                                  koff[e], soff, 0, 0);
     } else {  // ragged last block: rows past L repeat row L-1 (masked later)
+      const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e) {
-        const int r = min(krow[e], L - 1 - j * 128);
+        const int row = krow_of(w, e, lane);
+        const int r = min(row, L - 1 - j * 128);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
-                                                 (uint32_t)(r * k_row + kchunk[e] * 16), soff, 0, 0);
+                                                 (uint32_t)(r * k_row + kchunk_of(row, lane) * 16), soff, 0, 0);
       }
     }
   }
@@ -475,13 +491,19 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
 
   // The kept list is read 64 entries at a time into one VGPR (lane e holds
   // entry base + e) and entries are taken with readlane: no per-tile memory
-  // wait, so in-flight tile prefetches are never drained for an index.
-  int win = lst[min(lane, cnt - 1)];
+  // wait, so in-flight tile prefetches are never drained for an index.  The
+  // window is read through a buffer resource bounded by the row's capacity
+  // (i + 1 entries; reads past it return 0), so the first window does not
+  // wait for the count: both loads are in flight together.  Entries at or
+  // past the count are never selected.
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(lst), 0, (i + 1) * 4, 0x00020000);
+  int win = (int)__builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, 0, 0);
   int wbase = 0;
   auto entry = [&](int n) -> int {
     if (n - wbase >= 64) {  // rare: wait right here, so no wait sits on the common path
       wbase += 64;
-      win = lst[min(wbase + lane, cnt - 1)];
+      win = (int)__builtin_amdgcn_raw_buffer_load_b32(lrs, (wbase + lane) * 4, 0, 0);
       FP_WAIT_VMEM();
     }
     return __builtin_amdgcn_readlane(win, n - wbase);
@@ -609,22 +631,37 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ws.m - m);
   const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
   const float inv = a.out_scale / (l0 * a0 + l1 * a1);
-  if (tq < a.L) {
-    uint16_t* op = a.out + (int64_t)tq * a.o_st + (int64_t)h * a.o_sh;
+  const float w0 = a0 * inv, w1 = a1 * inv;
+  // A lane holds 4-dim pieces of one token; stored directly, every store
+  // instruction would touch 32 tokens one output row apart.  The bf16 rows
+  // of this wave's 32 tokens are staged in LDS (272-byte rows: 16-byte
+  // aligned, neighbouring rows on different banks) and written back as
+  // whole 256-byte head slices, four tokens per 1 KiB store instruction.
+  uint8_t* stg = reinterpret_cast<uint8_t*>(smem) + kMergeBytes + qg * 32 * kStageRow;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dt + 8 * q4 + 4 * hh;
-        uint32_t b[4];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * hh;
+      float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          const float v = (ws.o[dt][r] * a0 + src[(2 + 16 * dt + r) * 64 + lane] * a1) * inv;
-          b[e] = fpk::f32_to_bf16_bits(v);
-        }
-        *reinterpret_cast<uint2*>(op + d0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e;
+        v[e] = ws.o[dt][r] * w0 + src[(2 + 16 * dt + r) * 64 + lane] * w1;
       }
+      // v_cvt_pk_bf16_f32: round to nearest even, branch free
+      const bf16x2 p01 = {(__bf16)v[0], (__bf16)v[1]}, p23 = {(__bf16)v[2], (__bf16)v[3]};
+      *reinterpret_cast<uint2*>(stg + qi * kStageRow + 2 * d0) =
+          make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+    }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int ch = it * 64 + lane;  // 16-byte chunk: token ch / 16, piece ch % 16
+    const int tok = ch >> 4;
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + tok * kStageRow + (ch & 15) * 16);
+    const int t = i * 128 + 32 * qg + tok;
+    if (t < a.L)
+      *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (ch & 15) * 8) = v;
   }
 }
 
