@@ -13,29 +13,33 @@
 // last stage is block-sparse attention over the identified blocks); GQA per
 // the FlashPrefill V2 abstract.
 //
-// One workgroup = one (q head h, query block i), 8 waves.  Wave w owns query
-// rows 32*(w%4) .. +31 and key half kh = w/4 (keys 64kh .. 64kh+63 of every
-// kept block); the two halves keep separate online-softmax states and are
-// merged through LDS at the end.  Two waves per SIMD let one wave's softmax
-// (VALU) run under the other's matrix-core work.
+// One workgroup = one (q head h, query block i): 4 waves, wave w owning query
+// rows 32w .. 32w+31.  The kept key blocks are walked in 64-key units (two
+// per block); per unit every wave computes its 32 x 64 logits and P.V over
+// those 64 keys, so a wave keeps one online-softmax state for its queries
+// and no cross-wave merge is needed.  A workgroup stages 16 KiB K and V^T
+// half tiles (64 KiB of LDS in all), so two workgroups share a compute unit:
+// their waves pair up on each SIMD and, having no barrier in common, fill
+// each other's waits (barrier skew, row start-up, epilogue).
 //
-// Per kept key block j (ascending list, the diagonal last):
-//   * the K tile [128 keys][128 dims] and the V^T tile [128 dims][128 keys]
-//     travel global -> LDS with global_load_lds_dwordx4 (no registers), double
-//     buffered: the next block's tiles are in flight while this one computes.
-//     Rows are 16 chunks of 16 B stored at chunk ^ f(row), f(r) = (r & 15) ^
-//     (((r >> 3) & 1) << 2), so the operand reads below hit distinct banks;
+// Per 64-key unit (ascending list, the diagonal block last):
+//   * the K half tile [64 keys][128 dims] and the V^T half tile [128 dims]
+//     [64 keys] travel global -> LDS with buffer_load ... lds (no
+//     registers), double buffered.  K rows are 16 chunks of 16 B stored at
+//     chunk ^ f(row), f(r) = (r & 15) ^ (((r >> 3) & 1) << 2); V^T rows are
+//     8 chunks stored at chunk ^ (row & 7); both make the operand reads below
+//     hit distinct banks;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: two 32-key sub-tiles, eight
 //     16-wide steps over the head dimension.  A lane column is one query, so
 //     a lane holds 32 of its query's logits and lane ^ 32 the rest.  K rows
 //     are fed in the order pm(m) (bits 2 and 3 of m swapped), which makes
 //     each lane's logits contiguous 8-key runs: the B operand of P.V as is;
 //   * online softmax in the exp2 domain with a lazy maximum: the running max
-//     is raised (and O, l rescaled) only when a tile's max exceeds it by more
+//     is raised (and O, l rescaled) only when a unit's max exceeds it by more
 //     than 8 (P <= 2^8 stays exact enough in bf16 and cannot overflow fp32);
 //   * O^T += V^T P^T, P packed to bf16 from the S^T registers.
 // The causal mask is applied on the diagonal block only.  1/l and the V
-// dequantisation scale are applied once, after the merge.
+// dequantisation scale are applied once, at the end.
 //
 // Work order: heavy (late) query blocks first; within every run of 8*G
 // consecutive workgroup ids, the G heads of one kv group at one query block
@@ -64,10 +68,9 @@ struct AttnArgs {
   float out_scale;
 };
 
-constexpr int kTileU4 = 128 * 16;  // one 128 x 256 B tile in uint4
-constexpr int kMergeBytes = 4 * 66 * 64 * 4;  // key-half merge area: [qg][m, l, 64 O rows][64 lanes] floats
-constexpr int kStageRow = 272;                 // staged bf16 output row (256 B + 16 B pad)
-static_assert(kMergeBytes % 16 == 0 && kMergeBytes + 4 * 32 * kStageRow <= 4 * kTileU4 * 16, "LDS epilogue fits");
+constexpr int kHalfU4 = 64 * 16;  // one half tile (64 x 256 B K, or 128 x 128 B V^T) in uint4
+constexpr int kStageRow = 272;     // staged bf16 output row (256 B + 16 B pad)
+static_assert(4 * 32 * kStageRow <= 4 * kHalfU4 * 16, "output staging fits in the tile buffers");
 constexpr float kLazy = 8.0f;      // lazy-max slack in log2 units
 
 __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int& h, int& i) {
@@ -155,8 +158,8 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
-// Causal mask of the diagonal block: key 64kh + 32kt + 16(r/8) + 8hh + r%8
-// of this wave's half is dropped for query 32qg + qi when it lies later.
+// Causal mask of the diagonal block: key 64hf + 32kt + 16(r/8) + 8hh + r%8
+// of unit half hf is dropped for query 32qg + qi when it lies later.
 __device__ __forceinline__ void mask_diag(floatx16* s, int qg, int kh, int qi, int hh) {
   const int qrel = 32 * qg + qi;
 #pragma unroll
@@ -248,10 +251,10 @@ struct StepCtx {
 // whose four products are twice as long, does sub-tile 0 (4 per slot).
 template <bool kFp8>
 __device__ __forceinline__ void phase1(const uint4* sKn, const QFrag<kFp8>& qf, const floatx16* s_cur,
-                                       floatx16* s_nxt, StepCtx& x, int kh, int hh, int pm) {
+                                       floatx16* s_nxt, StepCtx& x, int hh, int pm) {
   s_nxt[0] = (floatx16){0};
   s_nxt[1] = (floatx16){0};
-  const int r0 = 64 * kh + pm;  // sub-tile 1 is rows r0 + 32, same swizzle
+  const int r0 = pm;  // sub-tile 1 is rows r0 + 32, same swizzle
   if constexpr (!kFp8) {
     const uint4* k0 = sKn + r0 * 16;
     const int xs = swz(r0) ^ hh;
@@ -314,18 +317,19 @@ __device__ __forceinline__ void phase1(const uint4* sKn, const QFrag<kFp8>& qf, 
 }
 
 // Phase 2 of step n: O += P(n) V(n), slot m = key group u = m >> 2 times
-// head dims 32 (m & 3) .. +31.  V^T row 32 dt + qi has the same swizzle for
-// every dt, so one address per u serves a group.  Slots 0-7 finish P(n)'s
+// head dims 32 (m & 3) .. +31.  V^T row 32 dt + qi (eight 16-byte chunks of
+// 8 keys) has the same swizzle qi & 7 for every dt, so one address per u
+// serves a group.  Slots 0-7 finish P(n)'s
 // exponentials (bf16: sub-tile 1 values 8-15, ready before slot 12 reads
 // them; e4m3: all of sub-tile 1, two per slot), slots 8-15 take the row max
 // of S(n+1) for the next step.  Returns that max (this lane's half).
 template <bool kFp8>
 __device__ __forceinline__ float phase2(const uint4* sV, const floatx16* s_cur, const floatx16* s_nxt,
-                                        WaveState& ws, StepCtx& x, int kh, int qi, int hh) {
-  const int xv = (8 * kh) ^ hh ^ swz(qi);
-  const uint4* vr = sV + qi * 16;
+                                        WaveState& ws, StepCtx& x, int qi, int hh) {
+  const int xv = hh ^ (qi & 7);
+  const uint4* vr = sV + qi * 8;
   auto vread = [&](int m) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(&vr[(m & 3) * 512 + ((2 * (m >> 2)) ^ xv)]);
+    return *reinterpret_cast<const bf16x8*>(&vr[(m & 3) * 256 + ((2 * (m >> 2)) ^ xv)]);
   };
   bf16x8 va[4];
   va[0] = vread(0);
@@ -356,31 +360,34 @@ __device__ __forceinline__ float phase2(const uint4* sV, const floatx16* s_cur, 
   return fmaxf(mx0, mx1);
 }
 
-// S^T sub-tiles of this wave's 64 keys of one K tile (prologue only).
+// S^T of one 64-key unit (prologue only).
 template <bool kFp8>
-__device__ __forceinline__ void qk_tile(const uint4* sK, const QFrag<kFp8>& qf, floatx16* s,
-                                        int kh, int hh, int pm) {
+__device__ __forceinline__ void qk_unit(const uint4* sK, const QFrag<kFp8>& qf, floatx16* s, int hh,
+                                        int pm) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) s[kt] = qk_rows<kFp8>(sK, qf, 64 * kh + 32 * kt + pm, hh, (floatx16){0});
+  for (int kt = 0; kt < 2; ++kt) s[kt] = qk_rows<kFp8>(sK, qf, 32 * kt + pm, hh, (floatx16){0});
 }
 
-// Direct-to-LDS tile loads.  bf16 K and V^T rows are 256 B (16 chunks of
-// 16 B): wave w moves row quads 4w .. 4w+3, lane l filling slot l%16 of row
-// 16w + 4e + l/16 with the global chunk (l%16) ^ swz(row).  e4m3 K rows are
-// 128 B: wave w moves row octets 2w, 2w+1, lane l filling slot l%8 of row
-// 16w + 8e + l/8 with chunk (l%8) ^ swz8(row).
-//
-// The loads are buffer_load ... lds through a buffer resource per kv head:
-// the per-lane byte offsets are fixed for the whole workgroup and the key
-// block only moves the scalar offset, so a tile costs no vector address
-// arithmetic.  (Buffer loads also keep LDS-read waits exact: while a flat or
-// global LDS load is in flight the compiler can only wait for every LDS
-// read, which would serialise the operand prefetch of the matrix products.)
-// The host guarantees every offset of a kv head fits in 31 bits.
+// Direct-to-LDS loads of 64-key half tiles, each 16 KiB (e4m3 K: 8 KiB),
+// moved as 1 KiB loads (64 lanes x 16 B) with buffer_load ... lds.
+//   K: 64 rows of 256 B (16 chunks); load e of wave w fills rows
+//      16w + 4e + l/16, lane l writing slot l%16 with the global chunk
+//      (l%16) ^ swz(row).  e4m3 rows are 128 B (8 chunks): rows
+//      16w + 8e + l/8, slot l%8 <- chunk (l%8) ^ swz8(row).
+//   V^T: 128 rows (head dims) of 64 keys = 128 B (8 chunks of 8 keys);
+//      load e of wave w fills rows 32w + 8e + l/8, slot l%8 <- chunk
+//      (l%8) ^ (row & 7).
+// A buffer resource per kv head holds the base; the per-lane offsets are
+// fixed for the workgroup and a unit only moves the scalar offset, so a load
+// costs no vector address arithmetic.  (Buffer loads also keep LDS-read
+// waits exact: while a flat or global LDS load is in flight the compiler can
+// only wait for every LDS read, which would serialise the operand prefetch of
+// the matrix products.)  The host guarantees every offset of a kv head fits
+// in 31 bits.
 template <bool kFp8>
 struct TileLoader {
   static constexpr int kEsz = kFp8 ? 1 : 2;
-  static constexpr int kKLoads = kFp8 ? 2 : 4;  // K loads per wave per tile
+  static constexpr int kKLoads = kFp8 ? 2 : 4;  // K loads per wave per unit
   __amdgpu_buffer_rsrc_t krs;  // K of kv head g
   __amdgpu_buffer_rsrc_t vrs;  // V^T rows of kv head g
   int k_tile;                  // bytes between consecutive key blocks of K
@@ -388,7 +395,7 @@ struct TileLoader {
   uint32_t koff[kKLoads], voff[4];
   int L;
 
-  // key row and 16-byte chunk that load e of wave w, lane `lane` moves
+  // key row (of the half tile) and 16-byte chunk that K load e moves
   __device__ __forceinline__ static int krow_of(int w, int e, int lane) {
     return kFp8 ? 16 * w + 8 * e + (lane >> 3) : 16 * w + 4 * e + (lane >> 4);
   }
@@ -412,13 +419,14 @@ struct TileLoader {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * w + 4 * e + (lane >> 4);
-      voff[e] = (uint32_t)(row * a.Lpad * 2 + ((lane & 15) ^ swz(row)) * 16);
+      const int row = 32 * w + 8 * e + (lane >> 3);
+      voff[e] = (uint32_t)(row * a.Lpad * 2 + ((lane & 7) ^ (row & 7)) * 16);
     }
   }
-  __device__ __forceinline__ void load_k(uint4* sK, int j, int w) const {
-    const int soff = j * k_tile;
-    if (j * 128 + 128 <= L) {
+  // K half tile hf of key block j
+  __device__ __forceinline__ void load_k(uint4* sK, int j, int hf, int w) const {
+    if (j * 128 + 64 * hf + 64 <= L) {
+      const int soff = j * k_tile + hf * 64 * k_row;
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
@@ -428,22 +436,24 @@ struct TileLoader {
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e) {
         const int row = krow_of(w, e, lane);
-        const int r = min(row, L - 1 - j * 128);
+        const int r = min(64 * hf + row, L - 1 - j * 128);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
-                                                 (uint32_t)(r * k_row + kchunk_of(row, lane) * 16), soff, 0, 0);
+                                                 (uint32_t)(r * k_row + kchunk_of(row, lane) * 16),
+                                                 j * k_tile, 0, 0);
       }
     }
   }
-  __device__ __forceinline__ void load_v(uint4* sV, int j, int w) const {
+  // V^T half tile hf of key block j (V^T is zero past L)
+  __device__ __forceinline__ void load_v(uint4* sV, int j, int hf, int w) const {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(sV + (4 * w + e) * 64), 16, voff[e],
-                                               j * 256, 0, 0);
+                                               j * 256 + hf * 128, 0, 0);
   }
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
-// | vmcnt[15:14]): wait for vector memory only, leaving N loads in flight.
+// | vmcnt[15:14]): wait for vector memory only.
 #define FP_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70) /* vmcnt(0) */
 
 // Workgroup barrier of the tile pipeline.  Each wave first waits until at
@@ -463,26 +473,24 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 template <bool kFp8>
-__global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
-  // K tile m lives in sK[m & 1], V^T tile m in sV[m & 1]; K runs one tile
+__global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 waves per SIMD: two workgroups per CU
+  // K unit m lives in sK[m & 1], V^T unit m in sV[m & 1]; K runs one unit
   // ahead of V because S(n+1) = K(n+1) Q^T is issued before P(n) V(n).
-  __shared__ uint4 smem[4 * kTileU4];
+  __shared__ uint4 smem[4 * kHalfU4];
   uint4* const sK0 = smem;
-  uint4* const sK1 = smem + kTileU4;
-  uint4* const sV0 = smem + 2 * kTileU4;
-  uint4* const sV1 = smem + 3 * kTileU4;
+  uint4* const sK1 = smem + kHalfU4;
+  uint4* const sV0 = smem + 2 * kHalfU4;
+  uint4* const sV1 = smem + 3 * kHalfU4;
 
   int h, i;
   work_item(blockIdx.x, a.nb, a.Hq, a.Hkv, h, i);
   const int g = h / (a.Hq / a.Hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int qg = w & 3;
-  const int kh = w >> 2;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // = query group
   const int qi = lane & 31;
   const int hh = lane >> 5;
-  const int tq = i * 128 + 32 * qg + qi;
+  const int tq = i * 128 + 32 * w + qi;
   const int pm = (qi & 0x13) | ((qi & 4) << 1) | ((qi & 8) >> 1);
   const float c = a.scale_log2;
 
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   const int* lst = a.indices + fpk::tri_offset(h, i, a.nb);
 
   // The kept list is read 64 entries at a time into one VGPR (lane e holds
-  // entry base + e) and entries are taken with readlane: no per-tile memory
+  // entry base + e) and entries are taken with readlane: no per-unit memory
   // wait, so in-flight tile prefetches are never drained for an index.  The
   // window is read through a buffer resource bounded by the row's capacity
   // (i + 1 entries; reads past it return 0), so the first window does not
@@ -539,6 +547,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
     }
   }
 
+  // Units: u = 0 .. 2 cnt - 1, unit u = half u & 1 of block list[u >> 1].
   // Load schedule.  Buffers: K(m) in sK[m & 1], V(m) in sV[m & 1].  Step n
   // computes S(n+1) from K(n+1) (phase 1) and O += P(n) V(n) (phase 2):
   //   after phase 1, a barrier frees K(n+1)'s buffer and K(n+3) is issued;
@@ -548,12 +557,13 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   // the wait leaves the two younger groups in flight (vmcnt(kK + kV)); near
   // the end of the list, where fewer groups are in flight, it waits for all.
   constexpr int kK = TileLoader<kFp8>::kKLoads;
-  int j0 = entry(0);
-  int j1 = cnt > 1 ? entry(1) : 0;
-  int j2 = cnt > 2 ? entry(2) : 0;
-  ld.load_k(sK0, j0, w);
-  ld.load_v(sV0, j0, w);
-  if (cnt > 1) ld.load_k(sK1, j1, w);
+  const int ucnt = 2 * cnt;
+  // block of units u, u+1, u+2 (two units per block: units 2b and 2b + 1)
+  int j0 = entry(0);  // block of unit 0 and unit 1
+  int j2 = cnt > 1 ? entry(1) : 0;  // block of units 2 and 3
+  ld.load_k(sK0, j0, 0, w);
+  ld.load_v(sV0, j0, 0, w);
+  ld.load_k(sK1, j0, 1, w);
   WaveState ws;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) ws.o[dt] = (floatx16){0};
@@ -562,22 +572,26 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
   FP_WAIT_VMEM();
   __syncthreads();
   floatx16 sA[2], sB[2];
-  qk_tile<kFp8>(sK0, qf, sA, kh, hh, pm);
+  qk_unit<kFp8>(sK0, qf, sA, hh, pm);
   __syncthreads();
-  if (cnt > 2) ld.load_k(sK0, j2, w);  // issued as step -1's phase-1 load
-  if (cnt > 1) ld.load_v(sV1, j1, w);  // and as its phase-2 load
-  if (j0 == i) mask_diag(sA, qg, kh, qi, hh);
+  if (ucnt > 2) ld.load_k(sK0, j2, 0, w);  // unit 2 (issued as step -1's phase-1 load)
+  ld.load_v(sV1, j0, 1, w);                // unit 1 (and as its phase-2 load)
+  if (j0 == i) mask_diag(sA, w, 0, qi, hh);
   float mx = pair_max(tile_max(sA));
 
+  // blocks of the units around step t: jb[0] = block of unit t, ...
+  // (t even: units t, t+1 share block jc; t+2, t+3 share block jn)
+  int jc = j0;   // block of units t and t+1 when t is even
+  int jn = j2;   // block of units t+2 and t+3
   StepCtx x;
   x.c = c;
-  int jn3 = 0;
-  // Two steps per trip so buffer and register roles are static.
-  for (int n = 0; n < cnt; n += 2) {
+  // Two steps (= one key block) per trip so buffer and register roles are
+  // static: half 0 is the block's first unit, half 1 its second.
+  for (int n = 0; n < ucnt; n += 2) {
+    int jn2 = 0;  // block of units n+4, n+5
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int t = n + half;  // this step
-      if (half == 1 && t >= cnt) break;
+      const int t = n + half;  // this step's unit
       floatx16* s_cur = half == 0 ? sA : sB;
       floatx16* s_nxt = half == 0 ? sB : sA;
       uint4* sKn = half == 0 ? sK1 : sK0;
@@ -585,72 +599,55 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
       raise_max(ws, mx, c);
       x.mu = ws.m == -INFINITY ? 0.0f : ws.m;
       x.l = ws.l;
-      phase1<kFp8>(sKn, qf, s_cur, s_nxt, x, kh, hh, pm);
+      phase1<kFp8>(sKn, qf, s_cur, s_nxt, x, hh, pm);
       // V(t) must have landed; K(t+2) and V(t+1) may still be in flight
-      if (t + 2 < cnt) tile_barrier<kK + 4>();
+      if (t + 2 < ucnt) tile_barrier<kK + 4>();
       else tile_barrier<0>();
-      if (t + 3 < cnt) {
-        jn3 = entry(t + 3);
-        ld.load_k(sKn, jn3, w);
+      // K(t+3): unit t+3 is half (t+3)&1 of block (t+3)>>1
+      if (t + 3 < ucnt) {
+        if (half == 0) ld.load_k(sKn, jn, 1, w);  // t even: unit t+3 = second half of jn
+        else {
+          jn2 = entry((t + 3) >> 1);  // t odd: unit t+3 = first half of the block after jn
+          ld.load_k(sKn, jn2, 0, w);
+        }
       }
-      mx = phase2<kFp8>(sVc, s_cur, s_nxt, ws, x, kh, qi, hh);
+      mx = phase2<kFp8>(sVc, s_cur, s_nxt, ws, x, qi, hh);
       ws.l = x.l;
-      if (t + 1 < cnt && j1 == i) {
-        mask_diag(s_nxt, qg, kh, qi, hh);
+      // S(t+1) belongs to unit t+1: block jc (t even) or jn (t odd)
+      const int jnext = half == 0 ? jc : jn;
+      if (t + 1 < ucnt && jnext == i) {
+        mask_diag(s_nxt, w, half == 0 ? 1 : 0, qi, hh);
         mx = tile_max(s_nxt);
       }
       mx = pair_max(mx);
       // K(t+2) must have landed; V(t+1) and K(t+3) may still be in flight
-      if (t + 3 < cnt) tile_barrier<kK + 4>();
+      if (t + 3 < ucnt) tile_barrier<kK + 4>();
       else tile_barrier<0>();
-      if (t + 2 < cnt) ld.load_v(sVc, j2, w);
-      j0 = j1;
-      j1 = j2;
-      j2 = jn3;
+      // V(t+2): unit t+2 is half t&1 of block jn
+      if (t + 2 < ucnt) ld.load_v(sVc, jn, half, w);
     }
+    jc = jn;
+    jn = jn2;
   }
 
-  // merge the two key halves of each query group through LDS
-  float* mrg = reinterpret_cast<float*>(sK0);  // [qg][66][64] floats over sK0..sV1
-  if (kh == 1) {
-    float* dst = mrg + qg * 66 * 64;
-    dst[lane] = ws.m;
-    dst[64 + lane] = ws.l;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(2 + 16 * dt + r) * 64 + lane] = ws.o[dt][r];
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  const float* src = mrg + qg * 66 * 64;
-  const float m1 = src[lane];
-  const float l1 = src[64 + lane] + src[64 + (lane ^ 32)];
-  const float l0 = ws.l + __shfl_xor(ws.l, 32);
-  const float m = fmaxf(ws.m, m1);
-  const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ws.m - m);
-  const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-  const float inv = a.out_scale / (l0 * a0 + l1 * a1);
-  const float w0 = a0 * inv, w1 = a1 * inv;
-  // A lane holds 4-dim pieces of one token; stored directly, every store
-  // instruction would touch 32 tokens one output row apart.  The bf16 rows
-  // of this wave's 32 tokens are staged in LDS (272-byte rows: 16-byte
-  // aligned, neighbouring rows on different banks) and written back as
-  // whole 256-byte head slices, four tokens per 1 KiB store instruction.
-  uint8_t* stg = reinterpret_cast<uint8_t*>(smem) + kMergeBytes + qg * 32 * kStageRow;
+  // Normalise and write out.  A lane holds 4-dim pieces of one token; stored
+  // directly, every store instruction would touch 32 tokens one output row
+  // apart.  The bf16 rows of this wave's 32 tokens are staged in LDS
+  // (272-byte rows: 16-byte aligned, neighbouring rows on different banks,
+  // over the tile buffers, which the last barrier has released) and written
+  // back as whole 256-byte head slices, four tokens per 1 KiB store.
+  const float l = ws.l + __shfl_xor(ws.l, 32);
+  const float inv = a.out_scale / l;
+  uint8_t* stg = reinterpret_cast<uint8_t*>(smem) + w * 32 * kStageRow;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * dt + 8 * q4 + 4 * hh;
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q4 + e;
-        v[e] = ws.o[dt][r] * w0 + src[(2 + 16 * dt + r) * 64 + lane] * w1;
-      }
+      const int r = 4 * q4;
       // v_cvt_pk_bf16_f32: round to nearest even, branch free
-      const bf16x2 p01 = {(__bf16)v[0], (__bf16)v[1]}, p23 = {(__bf16)v[2], (__bf16)v[3]};
+      const bf16x2 p01 = {(__bf16)(ws.o[dt][r] * inv), (__bf16)(ws.o[dt][r + 1] * inv)};
+      const bf16x2 p23 = {(__bf16)(ws.o[dt][r + 2] * inv), (__bf16)(ws.o[dt][r + 3] * inv)};
       *reinterpret_cast<uint2*>(stg + qi * kStageRow + 2 * d0) =
           make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
     }
@@ -659,7 +656,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(AttnArgs a) {
     const int ch = it * 64 + lane;  // 16-byte chunk: token ch / 16, piece ch % 16
     const int tok = ch >> 4;
     const uint4 v = *reinterpret_cast<const uint4*>(stg + tok * kStageRow + (ch & 15) * 16);
-    const int t = i * 128 + 32 * qg + tok;
+    const int t = i * 128 + 32 * w + tok;
     if (t < a.L)
       *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (ch & 15) * 8) = v;
   }
@@ -693,8 +690,8 @@ hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int
   a.out_scale = fp8 ? p.v_scale : 1.0f;
   const dim3 grid((unsigned)(dm.nb * dm.Hq));
   if (fp8)
-    hipLaunchKernelGGL(attn_d128_kernel<true>, grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL(attn_d128_kernel<true>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_d128_kernel<false>, grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL(attn_d128_kernel<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
