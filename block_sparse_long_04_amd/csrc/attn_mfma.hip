@@ -161,13 +161,18 @@ __device__ __forceinline__ float pair_max(float x) {
 // Causal mask of the diagonal block: key 64hf + 32kt + 16(r/8) + 8hh + r%8
 // of unit half hf is dropped for query 32qg + qi when it lies later.
 __device__ __forceinline__ void mask_diag(floatx16* s, int qg, int kh, int qi, int hh) {
-  const int qrel = 32 * qg + qi;
+  // key offset 32kt + 16(r/8) + r%8 is dropped when it exceeds lim.  The
+  // opaque copy keeps the compiler from hoisting the 32 comparisons out of
+  // the loop as lane masks (64 scalar registers for a path taken twice per
+  // row).
+  int lim = 32 * qg + qi - 64 * kh - 8 * hh;
+  asm volatile("" : "+v"(lim));
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int krel = 64 * kh + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
-      if (krel > qrel) s[kt][r] = -INFINITY;
+      const int koff = 32 * kt + 16 * (r >> 3) + (r & 7);
+      if (koff > lim) s[kt][r] = -INFINITY;
     }
 }
 
