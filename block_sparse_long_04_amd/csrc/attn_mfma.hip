@@ -27,8 +27,9 @@
 //     [64 keys] travel global -> LDS with buffer_load ... lds (no
 //     registers), double buffered.  K rows are 16 chunks of 16 B stored at
 //     chunk ^ f(row), f(r) = (r & 15) ^ (((r >> 3) & 1) << 2); V^T rows are
-//     8 chunks stored at chunk ^ (row & 7); both make the operand reads below
-//     hit distinct banks;
+//     8 chunks stored at chunk ^ ((row >> 1) & 7).  A 16-byte LDS read is
+//     served 16 lanes at a time over 64 four-byte banks; the swizzles give
+//     the 16 rows such a read touches 16 different 16-byte bank slots;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: two 32-key sub-tiles, eight
 //     16-wide steps over the head dimension.  A lane column is one query, so
 //     a lane holds 32 of its query's logits and lane ^ 32 the rest.  K rows
@@ -97,8 +98,9 @@ __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int&
 }
 
 __device__ __forceinline__ int swz(int row) { return (row & 15) ^ (((row >> 3) & 1) << 2); }
-// e4m3 K rows are 128 B (8 chunks): the chunk XOR (row >> 1) & 7 sends the 16
-// rows one operand read touches to 16 different bank groups.
+// 128-byte rows (e4m3 K, V^T half tiles) hold 8 chunks: the chunk XOR
+// (row >> 1) & 7 sends the 16 rows one operand read touches to 16 different
+// bank slots (row parity picks the 128-byte half of the 256-byte bank cycle).
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 using fpk::intx8;
@@ -323,15 +325,15 @@ __device__ __forceinline__ void phase1(const uint4* sKn, const QFrag<kFp8>& qf, 
 
 // Phase 2 of step n: O += P(n) V(n), slot m = key group u = m >> 2 times
 // head dims 32 (m & 3) .. +31.  V^T row 32 dt + qi (eight 16-byte chunks of
-// 8 keys) has the same swizzle qi & 7 for every dt, so one address per u
-// serves a group.  Slots 0-7 finish P(n)'s
+// 8 keys) has the same swizzle for every dt, so one address per u serves a
+// group.  Slots 0-7 finish P(n)'s
 // exponentials (bf16: sub-tile 1 values 8-15, ready before slot 12 reads
 // them; e4m3: all of sub-tile 1, two per slot), slots 8-15 take the row max
 // of S(n+1) for the next step.  Returns that max (this lane's half).
 template <bool kFp8>
 __device__ __forceinline__ float phase2(const uint4* sV, const floatx16* s_cur, const floatx16* s_nxt,
                                         WaveState& ws, StepCtx& x, int qi, int hh) {
-  const int xv = hh ^ (qi & 7);
+  const int xv = hh ^ swz8(qi);  // swz8(32 dt + qi) == swz8(qi)
   const uint4* vr = sV + qi * 8;
   auto vread = [&](int m) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(&vr[(m & 3) * 256 + ((2 * (m >> 2)) ^ xv)]);
@@ -381,7 +383,7 @@ __device__ __forceinline__ void qk_unit(const uint4* sK, const QFrag<kFp8>& qf, 
 //      16w + 8e + l/8, slot l%8 <- chunk (l%8) ^ swz8(row).
 //   V^T: 128 rows (head dims) of 64 keys = 128 B (8 chunks of 8 keys);
 //      load e of wave w fills rows 32w + 8e + l/8, slot l%8 <- chunk
-//      (l%8) ^ (row & 7).
+//      (l%8) ^ swz8(row).
 // A buffer resource per kv head holds the base; the per-lane offsets are
 // fixed for the workgroup and a unit only moves the scalar offset, so a load
 // costs no vector address arithmetic.  (Buffer loads also keep LDS-read
@@ -425,7 +427,7 @@ struct TileLoader {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 32 * w + 8 * e + (lane >> 3);
-      voff[e] = (uint32_t)(row * a.Lpad * 2 + ((lane & 7) ^ (row & 7)) * 16);
+      voff[e] = (uint32_t)(row * a.Lpad * 2 + ((lane & 7) ^ swz8(row)) * 16);
     }
   }
   // K half tile hf of key block j
