@@ -42,12 +42,8 @@
 // The causal mask is applied on the diagonal block only.  1/l and the V
 // dequantisation scale are applied once, at the end.
 //
-// Work order: heavy (late) query blocks first; within every run of 8*G
-// consecutive workgroup ids, the G heads of one kv group at one query block
-// get ids the hardware deals to the same XCD (ids go round-robin over the 8
-// XCDs), so a K/V tile fetched for one head is found in that XCD's L2 by the
-// other heads of its group.  The group-to-XCD assignment rotates with the
-// query block so that no XCD is left with one group's whole workload.
+// Work order: heavy (late) query blocks first, and the workgroups one XCD
+// runs together belong to one kv group (work_item below).
 #include "common.h"
 
 namespace {
@@ -74,27 +70,35 @@ constexpr int kStageRow = 272;     // staged bf16 output row (256 B + 16 B pad)
 static_assert(4 * 32 * kStageRow <= 4 * kHalfU4 * 16, "output staging fits in the tile buffers");
 constexpr float kLazy = 8.0f;      // lazy-max slack in log2 units
 
+// Workgroup id -> (head h, query block i).  Ids are dealt round-robin to the
+// 8 XCDs (id % 8), and each XCD holds 64 workgroups at a time (32 CUs x 2).
+// With 8 kv heads, XCD x takes kv group (x + t) % 8 for the 16 query blocks
+// of period t (its G heads each), so the workgroups an XCD runs together
+// share their kv group's K/V tiles in its L2, and the rotation spreads every
+// group over all XCDs.  Heavy (late) query blocks first.  Other head layouts,
+// and the rows after the last whole period, take plain row-major order.
+constexpr int kPeriodRows = 16;
 __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int& h, int& i) {
   const int G = Hq / Hkv;
-  const int total = nb * Hq;
-  const int chunk = 8 * G;
-  const int full = (total / chunk) * chunk;
-  int p, slot;
+  const int per = 8 * G * kPeriodRows;
+  const int full = Hkv == 8 ? (nb * Hq / per) * per : 0;
+  int row, grp, slot;
   if (bid < full) {
-    // run `sup` of 8*G ids: XCD x (= id % 8) gets (row, group) pair
-    // sup*8 + (x + sup) % 8 with its G heads; the rotation spreads every kv
-    // group over all XCDs, so per-group differences in kept work even out.
-    const int sup = bid / chunk;
-    const int r = bid - sup * chunk;
-    p = sup * 8 + (((r & 7) + sup) & 7);
-    slot = r >> 3;
+    const int x = bid & 7;
+    const int n = bid >> 3;
+    const int t = n / (G * kPeriodRows);
+    const int k = n - t * (G * kPeriodRows);
+    grp = (x + t) & 7;
+    row = t * kPeriodRows + k / G;
+    slot = k - (k / G) * G;
   } else {
-    p = bid / G;
+    const int p = bid / G;
     slot = bid - p * G;
+    row = p / Hkv;
+    grp = p - row * Hkv;
   }
-  const int row = p / Hkv;
   i = nb - 1 - row;
-  h = (p - row * Hkv) * G + slot;
+  h = grp * G + slot;
 }
 
 __device__ __forceinline__ int swz(int row) { return (row & 15) ^ (((row >> 3) & 1) << 2); }
