@@ -622,7 +622,12 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
           ld.load_k(sKn, jn2, 0, w);
         }
       }
+      // The two waves sharing a SIMD come from different workgroups; raising
+      // the issue priority of the matrix-heavy phase 2 lets the other wave's
+      // VALU-heavy phase 1 fill its gaps rather than compete for them.
+      __builtin_amdgcn_s_setprio(2);
       mx = phase2<kFp8>(sVc, s_cur, s_nxt, ws, x, qi, hh);
+      __builtin_amdgcn_s_setprio(0);
       ws.l = x.l;
       // S(t+1) belongs to unit t+1: block jc (t even) or jn (t odd)
       const int jnext = half == 0 ? jc : jn;
