@@ -9,165 +9,299 @@
 // block's softmax weight is at least tau times the row's largest; the
 // diagonal block is always kept.
 //
-// One workgroup (4 waves) owns 16 consecutive query-block rows of one q head.
+// Work split.  Row tiles are 16 consecutive query-block rows.  They are
+// taken in pairs (2p, 2p+1), and one workgroup (4 waves) owns pair a and pair
+// npairs-1-a of one q head: a short pair near the top of the causal triangle
+// and a long one near the bottom, so every workgroup scores the same number
+// of block pairs and no CU ends up with several long rows.
 // Scores are 16x16 tiles from the fp32 matrix cores (v_mfma_f32_16x16x4f32):
-// A = 16 pooled query rows, B = 16 pooled key rows, all of the head dimension.
-// Pass 1 takes the row maxima (waves stride over key tiles, meet in LDS);
-// pass 2 recomputes the identical tiles (same instruction order, so the same
-// bits) and turns the comparison into 16-bit keep masks per (row, key tile)
-// held in LDS; pass 3 compacts each row's mask with popcount + a wave-wide
-// exclusive scan and writes the ascending list.  Only kept entries reach HBM.
+// A = 16 pooled query rows, B = 16 pooled key rows, all of the head
+// dimension.  Every wave holds the A operands of all four row tiles (slots
+// u = 0..3), so a key tile it loads feeds four accumulation chains while all
+// four need it and the long pair's two afterwards.  Waves stride over key
+// tiles; the next tile's rows load while the current one is multiplied.
+// Pass 1 takes the row maxima (lanes of a DPP row, then waves via LDS);
+// pass 2 recomputes the identical tiles (same instruction sequence, so the
+// same bits) and turns the comparison into 16-bit keep masks per (row, key
+// tile) held in LDS; pass 3 compacts each row's mask one nonzero 64-column
+// word at a time (a lane per column, positions from the count of set bits
+// below the lane) and writes the ascending list with contiguous stores.  Only
+// kept entries reach HBM.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
 
 using fpk::floatx4;
 
+// Max over the 16 lanes of each DPP row: quad swaps (xor 1, xor 2), then
+// rotations by 4 and 8 within the row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false)));  // quad_perm 1,0,3,2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false)));  // quad_perm 2,3,0,1
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));  // row_ror 4
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));  // row_ror 8
+  return x;
+}
+
+constexpr int kSlots = 4;  // row tiles per workgroup (two pairs, 64 rows)
+
+// Mask entries per LDS row: the key tiles, rounded up to whole 64-column
+// words so pass 3 reads a word with one 8-byte load.
+__host__ __device__ __forceinline__ int mask_stride(int ntiles) { return (ntiles + 3) & ~3; }
+
 template <int D>
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qp,
-                                                     const float* __restrict__ kp, int Hq, int Hkv,
-                                                     int nb, float scale, float ln_tau, int dense,
-                                                     float* __restrict__ row_max,
-                                                     int* __restrict__ counts,
-                                                     int* __restrict__ indices) {
-  extern __shared__ uint16_t kmask[];  // [16 rows][ntiles]
-  __shared__ float red[4][16];
+__global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict__ qp,
+                                                        const float* __restrict__ kp, int Hq, int Hkv,
+                                                        int nb, float scale, float ln_tau, int dense,
+                                                        float* __restrict__ row_max,
+                                                        int* __restrict__ counts,
+                                                        int* __restrict__ indices) {
+  extern __shared__ uint16_t kmask[];  // [64 local rows][mask_stride]
+  __shared__ float red[4][16 * kSlots];
+  __shared__ __align__(16) float mrow[16 * kSlots];  // row maxima of the 64 local rows
 
   const int ntiles = (nb + 15) >> 4;
-  const int rt = ntiles - 1 - (int)(blockIdx.x / Hq);  // longest rows first
-  const int h = blockIdx.x % Hq;
+  const int kst = mask_stride(ntiles);
+  const int npairs = (ntiles + 1) >> 1;
+  const int a = (int)(blockIdx.x / Hq);  // short pair
+  const int b = npairs - 1 - a;          // long pair (b == a: the middle pair alone)
+  const int h = (int)(blockIdx.x % Hq);
   const int g = h / (Hq / Hkv);
-  const int i0 = rt * 16;
+  const bool two = b != a;
+  const int lo_hi = min(2 * a + 1, ntiles - 1);            // last key tile of slots 0, 1
+  const int rt_hi = two ? min(2 * b + 1, ntiles - 1) : lo_hi;  // last key tile of the workgroup
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int grp = lane >> 4;
+  // Lane (c16, grp) holds S[i][j] with i = 16 rt_u + 4grp + r, j = 16jt + c16,
+  // so j <= i  <=>  dl - r <= 16 (rt_u - jt).
+  const int dl = c16 - 4 * grp;
+  auto slot_tile = [&](int u) { return u < 2 ? 2 * a + u : 2 * b + u - 2; };
 
-  // A operand: lane supplies Qbar[i0 + c16][16t + 4grp + c] in MFMA step (t, c).
-  floatx4 qa[D / 16];
-  {
-    const int qrow = min(i0 + c16, nb - 1);
+  // A operands: lane supplies Qbar[16 rt_u + c16][16t + 4grp + c] for slot u
+  // in MFMA step (t, c).  Without a long pair, slots 2, 3 repeat 0, 1 (their
+  // rows are never used).
+  floatx4 qa[kSlots][D / 16];
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int qrow = min(16 * slot_tile(u) + c16, nb - 1);
     const float* qptr = qp + ((int64_t)h * nb + qrow) * D + 4 * grp;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) qa[t] = *reinterpret_cast<const floatx4*>(qptr + 16 * t);
+    for (int t = 0; t < D / 16; ++t) qa[u][t] = *reinterpret_cast<const floatx4*>(qptr + 16 * t);
   }
-  const float* kbase = kp + (int64_t)g * nb * D + 4 * grp;
+  // Pooled keys of kv head g through a buffer resource: the intrinsic loads
+  // stay where they are issued, so the read-ahead is really ahead.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(kp + (int64_t)g * nb * D), 0, nb * D * (int)sizeof(float), 0x00020000);
 
-  // D layout: lane holds S[i0 + 4grp + r][16jt + c16], r = 0..3.
-  auto tile = [&](int jt) -> floatx4 {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int krow = min(jt * 16 + c16, nb - 1);
-    const float* kptr = kbase + (int64_t)krow * D;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const floatx4 kb = *reinterpret_cast<const floatx4*>(kptr + 16 * t);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t][0], kb[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t][1], kb[1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t][2], kb[2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t][3], kb[3], acc, 0, 0, 0);
-    }
-    return acc;
+  // B operand of key tile jt: lane supplies Kbar[16jt + c16][16t + 4grp + c].
+  // Rows past the last block are clamped to it (their columns are masked).
+  struct KRows {
+    floatx4 v[D / 16];
   };
+  auto load_rows = [&](int jt) -> KRows {
+    KRows r;
+    const int krow = min(jt * 16 + c16, nb - 1);
+    const int off = (krow * D + 4 * grp) * (int)sizeof(float);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      r.v[t] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * t, 0, 0));
+    return r;
+  };
+  // D layout: lane holds S[16 rt_u + 4grp + r][16jt + c16], r = 0..3.  The
+  // slots from U0 (0, or 2 for the long pair alone) to 3 are independent
+  // chains, interleaved; the sequence per (slot, jt) is the same in both
+  // passes, so the bits are too.
+  auto tiles = [&](const KRows& kr, floatx4 (&acc)[kSlots], auto u0c) {
+    constexpr int U0 = decltype(u0c)::value;
+#pragma unroll
+    for (int u = U0; u < kSlots; ++u) acc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int u = U0; u < kSlots; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[u][t][c], kr.v[t][c], acc[u], 0, 0, 0);
+  };
+  using All = std::integral_constant<int, 0>;   // key tile needed by all four slots
+  using Long = std::integral_constant<int, 2>;  // key tile needed by the long pair only
 
   // ---- pass 1: row maxima over j <= i
-  float mr[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int jt = w; jt <= rt; jt += 4) {
-    const floatx4 acc = tile(jt);
-    const int j = jt * 16 + c16;
+  float mr[kSlots][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * grp + r;
-      const float s = acc[r] * scale;
-      if (j <= i && i < nb) mr[r] = fmaxf(mr[r], s);
+  for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mr[u][r] = -INFINITY;
+  auto max_step = [&](const KRows& kr, int jt, auto u0c) {
+    constexpr int U0 = decltype(u0c)::value;
+    floatx4 acc[kSlots];
+    tiles(kr, acc, u0c);
+#pragma unroll
+    for (int u = U0; u < kSlots; ++u) {
+      const int lim = 16 * (slot_tile(u) - jt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (dl - r <= lim) mr[u][r] = fmaxf(mr[u][r], acc[u][r] * scale);
+    }
+  };
+  auto max_any = [&](const KRows& kr, int jt) {
+    if (jt <= lo_hi) max_step(kr, jt, All{});
+    else max_step(kr, jt, Long{});
+  };
+  // Two register sets in turn: tile jt + 4 loads while tile jt multiplies.
+  // The step for jt + 4 runs even past the last tile, which keeps the loads
+  // unconditional; there j > i for every row, so the causal test rejects all.
+  if (w <= rt_hi) {
+    KRows ka = load_rows(w);
+    for (int jt = w; jt <= rt_hi; jt += 8) {
+      const KRows kb = load_rows(jt + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      max_any(ka, jt);
+      ka = load_rows(jt + 8);
+      __builtin_amdgcn_sched_barrier(0);
+      max_any(kb, jt + 4);
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int u = 0; u < kSlots; ++u)
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) mr[r] = fmaxf(mr[r], __shfl_xor(mr[r], off));
-  }
+    for (int r = 0; r < 4; ++r) mr[u][r] = row16_max(mr[u][r]);
   if (c16 == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[w][4 * grp + r] = mr[r];
+    for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[w][16 * u + 4 * grp + r] = mr[u][r];
   }
   __syncthreads();
-  float m[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * grp + r;
-    m[r] = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
+  if (threadIdx.x < 16 * kSlots) {
+    const int row = threadIdx.x;
+    mrow[row] = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
+    const int u = row >> 4;
+    const int i = 16 * slot_tile(u) + (row & 15);
+    if ((u < 2 || two) && i < nb) row_max[(int64_t)h * nb + i] = mrow[row];
   }
-  if (w == 0 && c16 == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * grp + r;
-      if (i < nb) row_max[(int64_t)h * nb + i] = m[r];
-    }
-  }
+  __syncthreads();
 
-  // ---- pass 2: keep masks per (row, key tile)
-  for (int jt = w; jt <= rt; jt += 4) {
-    uint64_t bits[4];
-    const int j = jt * 16 + c16;
-    if (dense) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * grp + r;
-        bits[r] = __ballot(j <= i && i < nb);
-      }
-    } else {
-      const floatx4 acc = tile(jt);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * grp + r;
-        const float s = acc[r] * scale;
-        const bool keep = (j <= i && i < nb) && ((s - m[r] >= ln_tau) || j == i);
-        bits[r] = __ballot(keep);
-      }
-    }
+  // ---- pass 2: keep masks of (local row, key tile) for every key tile up
+  // to the row's own tile; entries past it are never read
+  auto put_masks = [&](int jt, int u, const uint64_t (&bits)[4]) {
     if (lane < 16) {
       const int rr = lane & 3;
-      const uint64_t b = rr == 0 ? bits[0] : rr == 1 ? bits[1] : rr == 2 ? bits[2] : bits[3];
-      kmask[lane * ntiles + jt] = (uint16_t)((b >> (16 * (lane >> 2))) & 0xffffu);
+      const uint64_t bb = rr == 0 ? bits[0] : rr == 1 ? bits[1] : rr == 2 ? bits[2] : bits[3];
+      kmask[(16 * u + lane) * kst + jt] = (uint16_t)((bb >> (16 * (lane >> 2))) & 0xffffu);
+    }
+  };
+  auto mask_step = [&](const KRows& kr, int jt, auto u0c) {  // stores only for jt <= rt_hi
+    constexpr int U0 = decltype(u0c)::value;
+    floatx4 acc[kSlots];
+    tiles(kr, acc, u0c);
+    // The row maxima come from LDS after the products are issued (a compiler
+    // barrier keeps the reads here): they are not held across the loop.
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int u = U0; u < kSlots; ++u) {
+      const int rt = slot_tile(u);
+      const int lim = 16 * (rt - jt);
+      const int rows_left = nb - 16 * rt;  // i < nb  <=>  4 grp + r < rows_left
+      const floatx4 mu = *reinterpret_cast<const floatx4*>(mrow + 16 * u + 4 * grp);
+      uint64_t bits[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = (dl - r <= lim && 4 * grp + r < rows_left) &&
+                          ((acc[u][r] * scale - mu[r] >= ln_tau) || dl - r == lim);
+        bits[r] = __ballot(keep);
+      }
+      if (jt <= rt_hi) put_masks(jt, u, bits);
+    }
+  };
+  auto mask_any = [&](const KRows& kr, int jt) {
+    if (jt <= lo_hi) mask_step(kr, jt, All{});
+    else mask_step(kr, jt, Long{});
+  };
+  if (w <= rt_hi) {
+    if (dense) {
+      for (int jt = w; jt <= rt_hi; jt += 4) {
+#pragma unroll
+        for (int u = 0; u < kSlots; ++u) {
+          const int rt = slot_tile(u);
+          if (jt > rt) continue;
+          const int lim = 16 * (rt - jt);
+          const int rows_left = nb - 16 * rt;
+          uint64_t bits[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bits[r] = __ballot(dl - r <= lim && 4 * grp + r < rows_left);
+          put_masks(jt, u, bits);
+        }
+      }
+    } else {
+      KRows ka = load_rows(w);
+      for (int jt = w; jt <= rt_hi; jt += 8) {
+        const KRows kb = load_rows(jt + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_any(ka, jt);
+        ka = load_rows(jt + 8);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_any(kb, jt + 4);
+      }
     }
   }
   __syncthreads();
 
-  // ---- pass 3: compaction, wave w owns rows 4w .. 4w+3
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * w + rr;
-    const int i = i0 + row;
-    if (i >= nb) break;
-    const int nwords = (i + 64) >> 6;  // 64-column words covering j = 0..i
-    int* out = indices + fpk::tri_offset(h, i, nb);
-    int base = 0;
-    for (int wd0 = 0; wd0 < nwords; wd0 += 64) {
-      const int wd = wd0 + lane;
-      uint64_t bw = 0;
-      if (wd < nwords) {
+  // ---- pass 3: compaction.  Wave w owns local rows w, w+4, ..., w+60: four
+  // rows of every slot, so short and long rows are shared evenly.
+  constexpr int kRows = 16 * kSlots / 4;
+  int base[kRows];
+  int row_i[kRows];
+  int nwords_max = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = 4 * wd + q;
-          if (t <= rt) bw |= (uint64_t)kmask[row * ntiles + t] << (16 * q);
-        }
-      }
-      const int cnt = __popcll(bw);
-      int incl = cnt;
+  for (int k = 0; k < kRows; ++k) {
+    const int lr = w + 4 * k;
+    const int u = lr >> 4;
+    const int i = 16 * slot_tile(u) + (lr & 15);
+    row_i[k] = (u < 2 || two) && i < nb ? i : -1;
+    base[k] = 0;
+    if (row_i[k] >= 0) nwords_max = max(nwords_max, (i + 64) >> 6);
+  }
+  for (int wd0 = 0; wd0 < nwords_max; wd0 += 64) {
+    const int wd = wd0 + lane;  // this lane's 64-column word: key tiles 4wd .. 4wd+3
+    uint64_t bw[kRows];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+    for (int k = 0; k < kRows; ++k) {
+      const int i = row_i[k];
+      bw[k] = 0;
+      if (i >= 0 && wd <= (i >> 6)) {
+        const uint2 x = *reinterpret_cast<const uint2*>(kmask + (w + 4 * k) * kst + 4 * wd);
+        const int valid = (i >> 4) - 4 * wd + 1;  // entries up to the row's own tile
+        const uint64_t v = ((uint64_t)x.y << 32) | x.x;
+        bw[k] = valid >= 4 ? v : v & ((uint64_t(1) << (16 * valid)) - 1);
       }
-      const int total = __shfl(incl, 63);
-      int pos = base + incl - cnt;
-      while (bw) {
-        const int b = __builtin_ctzll(bw);
-        out[pos++] = 64 * wd + b;
-        bw &= bw - 1;
-      }
-      base += total;
     }
-    if (lane == 0) counts[(int64_t)h * nb + i] = base;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      if (row_i[k] < 0) continue;
+      int* out = indices + fpk::tri_offset(h, row_i[k], nb);
+      int bs = base[k];
+      uint64_t nz = __ballot(bw[k] != 0);
+      while (nz) {
+        const int src = __builtin_ctzll(nz);
+        nz &= nz - 1;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bw[k], src);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bw[k] >> 32), src);
+        if ((((uint64_t)hi << 32 | lo) >> lane) & 1)
+          out[bs + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0))] = 64 * (wd0 + src) + lane;
+        bs += __popc(lo) + __popc(hi);
+      }
+      base[k] = bs;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < kRows; ++k)
+      if (row_i[k] >= 0) counts[(int64_t)h * nb + row_i[k]] = base[k];
   }
 }
 
@@ -177,9 +311,18 @@ hipError_t fpk_launch_select(const FpDims& dm, const float* q_pool, const float*
                              float sm_scale, float ln_tau, float* row_max, int* counts,
                              int* indices, hipStream_t st) {
   const int ntiles = (dm.nb + 15) / 16;
-  const size_t lds = ((size_t)16 * ntiles * sizeof(uint16_t) + 3) & ~(size_t)3;
+  const int npairs = (ntiles + 1) / 2;
+  const size_t lds = (size_t)16 * kSlots * mask_stride(ntiles) * sizeof(uint16_t);
   const int dense = ln_tau == -INFINITY ? 1 : 0;
-  dim3 grid((unsigned)(ntiles * dm.Hq));
+  dim3 grid((unsigned)((npairs + 1) / 2 * dm.Hq));
+  // 64 rows x nb bits of masks: up to 128 KiB at 16384 blocks, above the
+  // default 64 KiB dynamic LDS window, so raise the kernel's limit when needed.
+  if (lds > 65536) {
+    const void* fn = dm.d == 128 ? reinterpret_cast<const void*>(&select_kernel<128>)
+                                 : reinterpret_cast<const void*>(&select_kernel<64>);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   if (dm.d == 128)
     hipLaunchKernelGGL(select_kernel<128>, grid, dim3(256), lds, st, q_pool, k_pool, dm.Hq, dm.Hkv,
                        dm.nb, sm_scale, ln_tau, dense, row_max, counts, indices);
