@@ -9,17 +9,20 @@
 // block's softmax weight is at least tau times the row's largest; the
 // diagonal block is always kept.
 //
-// Work split.  Row tiles are 16 consecutive query-block rows.  They are
-// taken in pairs (2p, 2p+1), and one workgroup (4 waves) owns pair a and pair
-// npairs-1-a of one q head: a short pair near the top of the causal triangle
-// and a long one near the bottom, so every workgroup scores the same number
-// of block pairs and no CU ends up with several long rows.
+// Work split.  Row tiles are 16 consecutive query-block rows.  A workgroup
+// (4 waves) of one q head owns S row tiles (S = 4, 2 or 1, set by the host
+// so that there are enough workgroups to fill the chip).  For S = 4 the tiles
+// are taken in pairs (2p, 2p+1), and a workgroup owns pair a and pair
+// npairs-1-a: a short pair near the top of the causal triangle and a long one
+// near the bottom, so every workgroup scores the same number of block pairs
+// and no CU ends up with several long rows.  S = 2 pairs single tiles the
+// same way; S = 1 is one tile per workgroup, heaviest first.
 // Scores are 16x16 tiles from the fp32 matrix cores (v_mfma_f32_16x16x4f32):
 // A = 16 pooled query rows, B = 16 pooled key rows, all of the head
-// dimension.  Every wave holds the A operands of all four row tiles (slots
-// u = 0..3), so a key tile it loads feeds four accumulation chains while all
-// four need it and the long pair's two afterwards.  Waves stride over key
-// tiles; the next tile's rows load while the current one is multiplied.
+// dimension.  Every wave holds the A operands of all S row tiles (slots
+// u = 0..S-1), so a key tile it loads feeds S accumulation chains while all
+// need it and the long group's afterwards.  Waves stride over key tiles; the
+// next tile's rows load while the current one is multiplied.
 // Pass 1 takes the row maxima (lanes of a DPP row, then waves via LDS);
 // pass 2 recomputes the identical tiles (same instruction sequence, so the
 // same bits) and turns the comparison into 16-bit keep masks per (row, key
@@ -45,33 +48,40 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
-constexpr int kSlots = 4;  // row tiles per workgroup (two pairs, 64 rows)
+// Workgroups per q head for S row tiles per workgroup.
+__host__ __device__ __forceinline__ int groups_of(int ntiles, int S) {
+  const int P = S > 1 ? S / 2 : 1;  // tiles of one group (short or long)
+  const int ng = (ntiles + P - 1) / P;
+  return S > 1 ? (ng + 1) / 2 : ng;
+}
 
 // Mask entries per LDS row: the key tiles, rounded up to whole 64-column
 // words so pass 3 reads a word with one 8-byte load.
 __host__ __device__ __forceinline__ int mask_stride(int ntiles) { return (ntiles + 3) & ~3; }
 
-template <int D>
+template <int D, int kSlots>
 __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict__ qp,
                                                         const float* __restrict__ kp, int Hq, int Hkv,
                                                         int nb, float scale, float ln_tau, int dense,
                                                         float* __restrict__ row_max,
                                                         int* __restrict__ counts,
                                                         int* __restrict__ indices) {
-  extern __shared__ uint16_t kmask[];  // [64 local rows][mask_stride]
+  extern __shared__ uint16_t kmask[];  // [16 S local rows][mask_stride]
   __shared__ float red[4][16 * kSlots];
-  __shared__ __align__(16) float mrow[16 * kSlots];  // row maxima of the 64 local rows
+  __shared__ __align__(16) float mrow[16 * kSlots];  // row maxima of the local rows
 
   const int ntiles = (nb + 15) >> 4;
   const int kst = mask_stride(ntiles);
-  const int npairs = (ntiles + 1) >> 1;
-  const int a = (int)(blockIdx.x / Hq);  // short pair
-  const int b = npairs - 1 - a;          // long pair (b == a: the middle pair alone)
+  constexpr int P = kSlots > 1 ? kSlots / 2 : 1;  // row tiles per group
+  const int ngroups = (ntiles + P - 1) / P;
+  // short group (S = 1: the only one, heaviest first)
+  const int a = kSlots > 1 ? (int)(blockIdx.x / Hq) : ngroups - 1 - (int)(blockIdx.x / Hq);
+  const int b = kSlots > 1 ? ngroups - 1 - a : a;        // long group
   const int h = (int)(blockIdx.x % Hq);
   const int g = h / (Hq / Hkv);
-  const bool two = b != a;
-  const int lo_hi = min(2 * a + 1, ntiles - 1);            // last key tile of slots 0, 1
-  const int rt_hi = two ? min(2 * b + 1, ntiles - 1) : lo_hi;  // last key tile of the workgroup
+  const bool two = kSlots > 1 && b != a;                 // false: the short group alone
+  const int lo_hi = min(P * a + P - 1, ntiles - 1);      // last key tile of the short group
+  const int rt_hi = two ? min(P * b + P - 1, ntiles - 1) : lo_hi;  // last key tile of the workgroup
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int c16 = lane & 15;
@@ -79,11 +89,11 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
   // Lane (c16, grp) holds S[i][j] with i = 16 rt_u + 4grp + r, j = 16jt + c16,
   // so j <= i  <=>  dl - r <= 16 (rt_u - jt).
   const int dl = c16 - 4 * grp;
-  auto slot_tile = [&](int u) { return u < 2 ? 2 * a + u : 2 * b + u - 2; };
+  auto slot_tile = [&](int u) { return u < P ? P * a + u : P * b + u - P; };
 
   // A operands: lane supplies Qbar[16 rt_u + c16][16t + 4grp + c] for slot u
-  // in MFMA step (t, c).  Without a long pair, slots 2, 3 repeat 0, 1 (their
-  // rows are never used).
+  // in MFMA step (t, c).  Without a long group, its slots repeat the short
+  // group's (their rows are never used).
   floatx4 qa[kSlots][D / 16];
 #pragma unroll
   for (int u = 0; u < kSlots; ++u) {
@@ -112,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
     return r;
   };
   // D layout: lane holds S[16 rt_u + 4grp + r][16jt + c16], r = 0..3.  The
-  // slots from U0 (0, or 2 for the long pair alone) to 3 are independent
+  // slots from U0 (0, or P for the long group alone) to S-1 are independent
   // chains, interleaved; the sequence per (slot, jt) is the same in both
   // passes, so the bits are too.
   auto tiles = [&](const KRows& kr, floatx4 (&acc)[kSlots], auto u0c) {
@@ -127,8 +137,8 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
         for (int u = U0; u < kSlots; ++u)
           acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[u][t][c], kr.v[t][c], acc[u], 0, 0, 0);
   };
-  using All = std::integral_constant<int, 0>;   // key tile needed by all four slots
-  using Long = std::integral_constant<int, 2>;  // key tile needed by the long pair only
+  using All = std::integral_constant<int, 0>;   // key tile needed by every slot
+  using Long = std::integral_constant<int, P>;  // key tile needed by the long group only
 
   // ---- pass 1: row maxima over j <= i
   float mr[kSlots][4];
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
     mrow[row] = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
     const int u = row >> 4;
     const int i = 16 * slot_tile(u) + (row & 15);
-    if ((u < 2 || two) && i < nb) row_max[(int64_t)h * nb + i] = mrow[row];
+    if ((u < P || two) && i < nb) row_max[(int64_t)h * nb + i] = mrow[row];
   }
   __syncthreads();
 
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
   }
   __syncthreads();
 
-  // ---- pass 3: compaction.  Wave w owns local rows w, w+4, ..., w+60: four
+  // ---- pass 3: compaction.  Wave w owns local rows w, w+4, w+8, ...: four
   // rows of every slot, so short and long rows are shared evenly.
   constexpr int kRows = 16 * kSlots / 4;
   int base[kRows];
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
     const int lr = w + 4 * k;
     const int u = lr >> 4;
     const int i = 16 * slot_tile(u) + (lr & 15);
-    row_i[k] = (u < 2 || two) && i < nb ? i : -1;
+    row_i[k] = (u < P || two) && i < nb ? i : -1;
     base[k] = 0;
     if (row_i[k] >= 0) nwords_max = max(nwords_max, (i + 64) >> 6);
   }
@@ -311,23 +321,33 @@ hipError_t fpk_launch_select(const FpDims& dm, const float* q_pool, const float*
                              float sm_scale, float ln_tau, float* row_max, int* counts,
                              int* indices, hipStream_t st) {
   const int ntiles = (dm.nb + 15) / 16;
-  const int npairs = (ntiles + 1) / 2;
-  const size_t lds = (size_t)16 * kSlots * mask_stride(ntiles) * sizeof(uint16_t);
+  // Most row tiles per workgroup that still give a workgroup per CU (256
+  // CUs); below that, parallelism matters more than K-tile reuse.  (Measured
+  // at 8K / 32K / 128K / 256K: S = 1 / 2 / 4 / 4 is the fastest choice.)
+  constexpr int kMinGroups = 256;
+  int S = 4;
+  if (groups_of(ntiles, 4) * dm.Hq < kMinGroups) S = groups_of(ntiles, 2) * dm.Hq >= kMinGroups ? 2 : 1;
+  const size_t lds = (size_t)16 * S * mask_stride(ntiles) * sizeof(uint16_t);
   const int dense = ln_tau == -INFINITY ? 1 : 0;
-  dim3 grid((unsigned)((npairs + 1) / 2 * dm.Hq));
-  // 64 rows x nb bits of masks: up to 128 KiB at 16384 blocks, above the
-  // default 64 KiB dynamic LDS window, so raise the kernel's limit when needed.
-  if (lds > 65536) {
-    const void* fn = dm.d == 128 ? reinterpret_cast<const void*>(&select_kernel<128>)
-                                 : reinterpret_cast<const void*>(&select_kernel<64>);
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(groups_of(ntiles, S) * dm.Hq));
+  auto launch = [&](auto kern) -> hipError_t {
+    // 16 S rows x nb bits of masks: up to 128 KiB at 16384 blocks, above the
+    // default 64 KiB dynamic LDS window, so raise the kernel's limit when needed.
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, q_pool, k_pool, dm.Hq, dm.Hkv, dm.nb, sm_scale,
+                       ln_tau, dense, row_max, counts, indices);
+    return hipGetLastError();
+  };
+  if (dm.d == 128) {
+    if (S == 4) return launch(select_kernel<128, 4>);
+    if (S == 2) return launch(select_kernel<128, 2>);
+    return launch(select_kernel<128, 1>);
   }
-  if (dm.d == 128)
-    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(256), lds, st, q_pool, k_pool, dm.Hq, dm.Hkv,
-                       dm.nb, sm_scale, ln_tau, dense, row_max, counts, indices);
-  else
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(256), lds, st, q_pool, k_pool, dm.Hq, dm.Hkv,
-                       dm.nb, sm_scale, ln_tau, dense, row_max, counts, indices);
-  return hipGetLastError();
+  if (S == 4) return launch(select_kernel<64, 4>);
+  if (S == 2) return launch(select_kernel<64, 2>);
+  return launch(select_kernel<64, 1>);
 }

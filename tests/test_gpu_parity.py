@@ -15,7 +15,7 @@ import torch
 import oracle.flashprefill_oracle as O
 from block_sparse_long_04_amd import _lib
 from block_sparse_long_04_amd.inputs import CONFIGS, make_layer
-from tests.parity_util import (check_lists_wellformed, check_out, check_pool, oracle_full,
+from tests.parity_util import (check_lists_wellformed, check_out, check_pool, gpu_lists, oracle_full,
                                require_gpu, run_gpu, say, selection_mismatch, sm_scale)
 
 pytestmark = pytest.mark.gpu
@@ -186,3 +186,46 @@ def test_e4m3_decode_of_every_code_in_pool_and_vt():
     assert torch.equal(col[fin], want[fin])
     # zero padding past L
     assert torch.count_nonzero(vt[:, :, L:].float()).item() == 0
+
+
+# Selection at shapes that reach every work split of the selection kernel
+# (a workgroup owns 4, 2 or 1 tiles of 16 query-block rows, paired short
+# with long), with the odd cases: an odd number of tile pairs (the middle
+# pair alone), an odd number of tiles (the last pair has one tile), and a
+# ragged last tile and block.  Pooling, row maxima and kept sets against the
+# oracle (no attention: the oracle's selection is the part under test).
+SPLIT_CASES = {
+    # name: (overrides, tau); 32 q / 8 kv heads, B = 64
+    "four_tiles_odd_pairs": ({"seq_len": 464 * 64 + 51}, 0.1),      # nb 465: 30 tiles, 15 pairs
+    "four_tiles_odd_tiles": ({"seq_len": 488 * 64 + 37}, 0.05),     # nb 489: 31 tiles
+    "two_tiles_d64": ({"seq_len": 232 * 64 + 30, "head_dim": 64}, 0.1),  # nb 233: 15 tiles
+    "four_tiles_dense": ({"seq_len": 464 * 64 + 51}, 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_selection_work_splits(name):
+    dev = require_gpu()
+    over, tau = SPLIT_CASES[name]
+    cfg = CONFIGS["c3"].with_(block_size=64, **over)
+    nb = cfg.num_blocks
+    say(f"[split {name}] L={cfg.seq_len} nb={nb} d={cfg.head_dim} tau={tau}")
+    layer = make_layer(cfg)
+    ref = oracle_full(layer, tau, attention=False)
+    q, k, v = (t.to(dev) for t in (layer.q, layer.k, layer.v))
+    pf = _lib.Prefill(q, k, v, block_size=cfg.block_size, threshold=tau)
+    pf.pool()
+    pf.select()
+    torch.cuda.synchronize()
+    res = dict(qbar=pf.ws.q_pool().cpu().numpy(), kbar=pf.ws.k_pool().cpu().numpy())
+    check_pool(res, ref["qbar"], ref["kbar"])
+    np.testing.assert_allclose(pf.ws.row_max().cpu().numpy(), ref["row_max"], rtol=1e-5, atol=1e-5)
+    lists = gpu_lists(pf.ws.counts().cpu().numpy(), pf.ws.indices().cpu().numpy(), nb)
+    check_lists_wellformed(lists, nb)
+    bad, amb = selection_mismatch(lists, ref["keep"], ref["amb"])
+    say(f"    selection: {bad} mismatches outside the tie zone, {amb} inside")
+    assert bad == 0
+    if tau == 0.0:
+        for row in lists:
+            for i, lst in enumerate(row):
+                assert len(lst) == i + 1
