@@ -77,9 +77,28 @@ constexpr float kLazy = 8.0f;      // lazy-max slack in log2 units
 // share their kv group's K/V tiles in its L2, and the rotation spreads every
 // group over all XCDs.  Heavy (late) query blocks first.  Other head layouts,
 // and the rows after the last whole period, take plain row-major order.
+// Long sequences (nb >= 2048, a multiple of 128) instead take the kv groups
+// one after another: all XCDs work on one group (XCD x on a 16-row band of
+// every 128 rows, heavy rows first), so the K/V the chip touches at a time is
+// one group's, which the Infinity Cache holds (128 MiB at 256K tokens against
+// 1 GiB for all eight).  Each group then spans at least 16 rounds of 512
+// workgroups, so light rows still end the kernel only within each group.
 constexpr int kPeriodRows = 16;
+constexpr int kSeqGroupsMinBlocks = 2048;
 __device__ __forceinline__ void work_item(int bid, int nb, int Hq, int Hkv, int& h, int& i) {
   const int G = Hq / Hkv;
+  if (nb >= kSeqGroupsMinBlocks && nb % 128 == 0) {
+    const int x = bid & 7;
+    const int n = bid >> 3;
+    const int per_g = nb * G / 8;  // ids of one kv group per XCD
+    const int g = n / per_g;
+    const int m = n - g * per_g;
+    const int t = m / (16 * G);
+    const int k = m - t * (16 * G);
+    i = nb - 1 - (t * 128 + x * 16 + k / G);
+    h = g * G + (k - (k / G) * G);
+    return;
+  }
   const int per = 8 * G * kPeriodRows;
   const int full = Hkv == 8 ? (nb * Hq / per) * per : 0;
   int row, grp, slot;
