@@ -20,8 +20,10 @@ LIB_PATH = os.path.join(PKG_DIR, "libflashprefill.so")
 FP_F32, FP_BF16, FP_FP8_E4M3 = 0, 1, 2
 FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_sparse_prefill",
-            "fp_strerror")
+FP_SELECT_TOPK, FP_SELECT_TOPP = 1, 2
+
+EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_sorted",
+            "fp_sparse_prefill", "fp_strerror")
 
 
 class FpProblem(ctypes.Structure):
@@ -72,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.fp_block_select_sorted.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
+    lib.fp_block_select_sorted.restype = ctypes.c_int
     lib.fp_strerror.argtypes = [ctypes.c_int]
     lib.fp_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -106,6 +111,12 @@ def fp_block_pool(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> N
 def fp_block_select(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check(load_library().fp_block_select(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
            "fp_block_select")
+
+
+def fp_block_select_sorted(prob: FpProblem, rule: int, param: float, ws_ptr: int, ws_bytes: int,
+                           stream: int) -> None:
+    _check(load_library().fp_block_select_sorted(ctypes.byref(prob), rule, param, ws_ptr, ws_bytes,
+                                                 stream), "fp_block_select_sorted")
 
 
 def fp_sparse_prefill(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
@@ -255,6 +266,11 @@ class Prefill:
 
     def select(self):
         fp_block_select(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def select_sorted(self, rule: int, param: float):
+        """Top-k (rule FP_SELECT_TOPK, param = k) or top-p (FP_SELECT_TOPP,
+        param = p) selection into the same workspace sections as select()."""
+        fp_block_select_sorted(self.prob, rule, param, self.ws.ptr, self.ws.nbytes, self.stream())
 
     def attend(self):
         fp_sparse_prefill(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())

@@ -156,6 +156,30 @@ int fp_block_select(const fp_problem* p, void* workspace, size_t workspace_bytes
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 
+int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (rule == FP_SELECT_TOPK) {
+    if (!(param >= 1.0f && param <= 16777216.0f && param == floorf(param))) return FP_ERR_INVALID;
+  } else if (rule == FP_SELECT_TOPP) {
+    if (!(param > 0.0f && param <= 1.0f)) return FP_ERR_INVALID;
+  } else {
+    return FP_ERR_INVALID;
+  }
+  if (dm.nb > 2048) return FP_ERR_UNSUPPORTED;
+  if (dm.L == 0) return FP_OK;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const hipError_t e = fpk_launch_select_sorted(
+      dm, at<float>(workspace, w.q_pool), at<float>(workspace, w.k_pool), eff_sm_scale(p), rule, param,
+      at<float>(workspace, w.row_max), at<int>(workspace, w.counts), at<int>(workspace, w.indices),
+      (hipStream_t)stream);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
   FpDims dm;
   int rc = check_problem(p, &dm);

@@ -122,6 +122,24 @@ int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, 
  * block score matrix is never stored. */
 int fp_block_select(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Selection rules that sort the block scores or accumulate their mass: the
+ * baselines the single-pass threshold avoids (FlashPrefill skill page, "Core
+ * Concept"; FlashPrefill abstract).  Same sections as fp_block_select: reads
+ * q_pool and k_pool, writes row_max, counts and indices (so fp_sparse_prefill
+ * runs on the result), with another keep rule per row (h, i) over the causal
+ * blocks j <= i of the same scores S:
+ *   FP_SELECT_TOPK: the k (= param, a whole number >= 1) largest scores;
+ *   FP_SELECT_TOPP: the shortest prefix in descending score order whose block
+ *                   softmax mass exp(S - m) / sum exp(S - m) reaches p
+ *                   (= param, in (0, 1]);
+ * among equal scores the smaller block index first; the diagonal block is
+ * kept as well.  p->threshold is not used.  Rows are sorted whole in LDS, so
+ * nb <= 2048 (FP_ERR_UNSUPPORTED beyond); a bad rule or param is
+ * FP_ERR_INVALID. */
+typedef enum { FP_SELECT_TOPK = 1, FP_SELECT_TOPP = 2 } fp_select_rule;
+int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Step 5.  Reads q, k, v (or v_t, written by fp_block_pool), counts and
  * indices; writes out.  Must follow fp_block_pool on the same workspace. */
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);

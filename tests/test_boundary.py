@@ -154,3 +154,28 @@ def test_strerror_texts():
     for code in (0, -1, -2, -3, -4):
         assert fp.strerror(code)
     assert "unknown" in fp.strerror(12345)
+
+
+def test_sorted_selection_rejects_bad_rules_and_sizes_before_launch():
+    p = prob()
+    lay = fp.fp_workspace_layout(p)
+    fake = 1 << 20
+    p.q, p.k, p.v, p.out = fake, fake, fake, fake
+    for rule, param in ((fp.FP_SELECT_TOPK, 0.0), (fp.FP_SELECT_TOPK, 2.5), (fp.FP_SELECT_TOPK, -3.0),
+                        (fp.FP_SELECT_TOPP, 0.0), (fp.FP_SELECT_TOPP, 1.5),
+                        (fp.FP_SELECT_TOPP, float("nan")), (0, 1.0), (3, 1.0)):
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fp.fp_block_select_sorted(p, rule, param, fake, lay.total, 0)
+        assert e.value.code == fp.FP_ERR_INVALID, (rule, param)
+    # workspace checks as for the other entry points
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_block_select_sorted(p, fp.FP_SELECT_TOPK, 4.0, fake, lay.total - 1, 0)
+    assert e.value.code == fp.FP_ERR_WORKSPACE
+    # rows are sorted whole in LDS: more than 2048 blocks is unsupported
+    big = prob(seq_len=2049 * 128)
+    big.q, big.k, big.v, big.out = fake, fake, fake, fake
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_block_select_sorted(big, fp.FP_SELECT_TOPP, 0.9, fake, 1 << 40, 0)
+    assert e.value.code == fp.FP_ERR_UNSUPPORTED
+    # empty problem: nothing launched
+    fp.fp_block_select_sorted(prob(seq_len=0), fp.FP_SELECT_TOPK, 1.0, 0, 0, 0)
