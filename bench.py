@@ -10,8 +10,9 @@ bf16, tau = 0.1).
 
 Prints ONE JSON line: value = kept-block TFLOP/s over the whole step
 (algorithmic FLOPs of the kept (query, key) pairs / ms per layer), plus
-per-stage times, the attention kernel's roofline and the CPU oracle timed on
-a bounded sample of the same layer on this host.
+per-stage times, the attention kernel's roofline, the CPU oracle timed on a
+bounded sample of the same layer on this host, and (up to 2048 blocks) the
+sorting / cumulative-sum selection baselines timed next to the threshold.
 """
 from __future__ import annotations
 
@@ -211,6 +212,26 @@ def cpu_baseline(layer_dev, lists_gpu, counts, cfg, tau, budget_s):
     }
 
 
+def select_baselines(pf, _lib, torch, thr_ms, k, p, reps=5):
+    """Median device time of fp_block_select_sorted (top-k, top-p) against
+    the threshold selection of the same run."""
+    out = {"threshold_ms": round(thr_ms, 4)}
+    for name, rule, param in (("topk", _lib.FP_SELECT_TOPK, k), ("topp", _lib.FP_SELECT_TOPP, p)):
+        pf.select_sorted(rule, param)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pf.select_sorted(rule, param)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[reps // 2]
+        out[name] = {"param": param, "ms": round(ms, 4), "vs_threshold": round(ms / thr_ms, 2),
+                     "kept_blocks": int(pf.ws.counts().sum().item())}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -328,6 +349,13 @@ def main():
             return idx[o:o + int(counts[h, i])].cpu().numpy()
 
         res["cpu_baseline"] = cpu_baseline(layer, lists_gpu, counts, cfg, tau, args.cpu_seconds)
+    if nb <= 2048:
+        # the sorting / cumulative-sum selection rules the threshold replaces,
+        # on the same proxies, timed outside the step (top-k at the threshold's
+        # mean kept count, top-p at 0.9)
+        k_match = max(1, int(round(float(counts.mean()))))
+        res["select_baselines"] = select_baselines(pf, _lib, torch, stage_ms["select"], k_match, 0.9)
+        pf.select()  # leave the threshold's lists in the workspace
     print(json.dumps(res), flush=True)
 
 

@@ -18,12 +18,13 @@
 //      sequence of the threshold kernel (so the same bits), stored in LDS as
 //      order-preserving 32-bit keys, one row of pow2(nb) keys per query block,
 //      -inf past the diagonal.
-//   B. Each wave sorts four rows in place (bitonic, descending, the row
-//      length rounded up to a power of two) and finds the cut: top-k takes
-//      the k-th key; top-p weighs the sorted scores by exp(S - m), sums them
-//      (fp32, a contiguous chunk per lane, then a wave scan) and takes the
-//      first prefix reaching p times the total.  Blocks equal to the cut key
-//      fill the remaining places in ascending block order.
+//   B. Each wave sorts four rows, one at a time, in registers (bitonic,
+//      descending; the row length rounded up to a power of two, 64 E keys
+//      held E per lane) and finds the cut: top-k takes the k-th key; top-p
+//      weighs the sorted scores by exp(S - m), sums them (fp32, a contiguous
+//      chunk per lane, then a wave scan) and takes the first prefix reaching
+//      p times the total.  Blocks equal to the cut key fill the remaining
+//      places in ascending block order.
 //   C. The tiles are recomputed (same bits) and compared with the cut key:
 //      16-bit masks of blocks above it and of blocks equal to it.
 //   D. Compaction as in the threshold kernel, after taking the needed number
@@ -51,6 +52,120 @@ __host__ __device__ __forceinline__ int pow2_at_least(int n) {
   return p;
 }
 __host__ __device__ __forceinline__ int mask_stride(int ntiles) { return (ntiles + 3) & ~3; }
+
+// Bitonic sort of n = 64 E keys held E per lane (lane l: elements l E ..
+// l E + E - 1), descending.  In the stage (k, j) the element with index x
+// meets x ^ j; the lower of the two takes the larger key where bit k of x is
+// clear (a descending run), the smaller where it is set.  Strides below E
+// stay inside a lane's registers, longer ones swap with lane ^ (j / E).
+template <int E>
+__device__ __forceinline__ void sort_desc(uint32_t (&v)[E], int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64 * E; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & j) continue;
+          const int x = lane * E + e;
+          const bool desc = (x & k) == 0;
+          const uint32_t a = v[e], b = v[e | j];
+          v[e] = desc ? max(a, b) : min(a, b);
+          v[e | j] = desc ? min(a, b) : max(a, b);
+        }
+      } else {
+        const int lm = j / E;
+        const bool lower = (lane & lm) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t y = (uint32_t)__shfl_xor((int)v[e], lm);
+          const bool desc = ((lane * E + e) & k) == 0;
+          v[e] = (lower == desc) ? max(v[e], y) : min(v[e], y);
+        }
+      }
+    }
+  }
+}
+
+// Element x of the sorted row (x uniform over the wave): register x % E of
+// lane x / E, read with readlane from every register and combined with
+// masks, so that no register is indexed at run time.
+template <int E>
+__device__ __forceinline__ uint32_t element(const uint32_t (&v)[E], int x) {
+  const int src = x / E, e = x - src * E;
+  uint32_t r = 0;
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    const uint32_t vq = (uint32_t)__builtin_amdgcn_readlane((int)v[q], src);
+    r |= q == e ? vq : 0u;
+  }
+  return r;
+}
+
+// Sort row i (keys in LDS, n = 64 E entries, -inf past the row), find its
+// cut and return (cut key, blocks to take among those equal to it, row max).
+template <int E>
+__device__ void row_cut(const uint32_t* s, int i, int lane, int rule, float param, uint32_t& ck_out,
+                        int& need_out, float& m_out) {
+  uint32_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = s[lane * E + e];
+  sort_desc<E>(v, lane);
+  const float m = key_val((uint32_t)__builtin_amdgcn_readlane((int)v[0], 0));
+  int n_keep;
+  if (rule == 1) {
+    n_keep = min((int)param, i + 1);
+  } else {
+    // weights exp(S - m) of this lane's contiguous chunk, summed in order,
+    // then a wave scan; the lane whose chunk crosses p times the total walks it
+    float w[E];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      w[e] = __expf(key_val(v[e]) - m);
+      ps += w[e];
+    }
+    float incl = ps;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const float up = __shfl_up(incl, 1);  // every lane takes part in the exchange
+    const float excl = lane == 0 ? 0.f : up;
+    const float total = __shfl(incl, 63);
+    const float target = param * total;
+    const uint64_t hit = __ballot(incl >= target);
+    if (hit == 0) {
+      n_keep = i + 1;
+    } else {
+      const int L = __builtin_ctzll(hit);
+      int pos = lane * E + E - 1;
+      float acc = excl;
+      bool found = false;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        acc += w[e];
+        if (!found && acc >= target) {
+          pos = lane * E + e;
+          found = true;
+        }
+      }
+      n_keep = min(__shfl(pos, L) + 1, i + 1);
+    }
+  }
+  const int c = n_keep - 1;
+  const uint32_t ck = element<E>(v, c);
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) gt += v[e] > ck ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) gt += __shfl_xor(gt, off);
+  ck_out = ck;
+  need_out = n_keep - gt;
+  m_out = m;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void select_sorted_kernel(const float* __restrict__ qp,
@@ -120,70 +235,21 @@ __global__ __launch_bounds__(256) void select_sorted_kernel(const float* __restr
   for (int row = w; row < 16; row += 4) {
     const int i = i0 + row;
     if (i >= nb) break;
-    uint32_t* s = keys + row * rs;
-    const int n = pow2_at_least(i + 1);
-    for (int k = 2; k <= n; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int pr = lane; pr < (n >> 1); pr += 64) {
-          const int a = ((pr & ~(jj - 1)) << 1) | (pr & (jj - 1));
-          const int b = a | jj;
-          const uint32_t x = s[a], y = s[b];
-          const bool desc = (a & k) == 0;  // descending runs where bit k of a is clear
-          if (desc ? (x < y) : (x > y)) {
-            s[a] = y;
-            s[b] = x;
-          }
-        }
-        asm volatile("" ::: "memory");  // keep the stages in order (one wave: LDS is in order)
-      }
+    const uint32_t* s = keys + row * rs;
+    uint32_t ck;
+    int need;
+    float m;
+    switch (pow2_at_least(i + 1) >> 6) {
+      case 1: row_cut<1>(s, i, lane, rule, param, ck, need, m); break;
+      case 2: row_cut<2>(s, i, lane, rule, param, ck, need, m); break;
+      case 4: row_cut<4>(s, i, lane, rule, param, ck, need, m); break;
+      case 8: row_cut<8>(s, i, lane, rule, param, ck, need, m); break;
+      case 16: row_cut<16>(s, i, lane, rule, param, ck, need, m); break;
+      default: row_cut<32>(s, i, lane, rule, param, ck, need, m); break;
     }
-    const float m = key_val(s[0]);
-    int n_keep;
-    if (rule == 1) {
-      n_keep = min((int)param, i + 1);
-    } else {
-      // chunk of n / 64 sorted entries per lane; entries past the row are -inf (weight 0)
-      const int cl = n >> 6;
-      float ps = 0.f;
-      for (int q = 0; q < cl; ++q) ps += __expf(key_val(s[lane * cl + q]) - m);
-      float incl = ps;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const float up = __shfl_up(incl, 1);  // every lane takes part in the exchange
-      const float excl = lane == 0 ? 0.f : up;
-      const float total = __shfl(incl, 63);
-      const float target = param * total;
-      const uint64_t hit = __ballot(incl >= target);
-      if (hit == 0) {
-        n_keep = i + 1;
-      } else {
-        const int L = __builtin_ctzll(hit);
-        int pos = 0;
-        if (lane == L) {
-          float acc = excl;
-          pos = lane * cl + cl - 1;
-          for (int q = 0; q < cl; ++q) {
-            acc += __expf(key_val(s[lane * cl + q]) - m);
-            if (acc >= target) {
-              pos = lane * cl + q;
-              break;
-            }
-          }
-        }
-        n_keep = min(__shfl(pos, L) + 1, i + 1);
-      }
-    }
-    const uint32_t ck = s[n_keep - 1];
-    int gt = 0;
-    for (int q = lane; q < n; q += 64) gt += s[q] > ck ? 1 : 0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) gt += __shfl_xor(gt, off);
     if (lane == 0) {
       cut_key[row] = ck;
-      need_eq[row] = n_keep - gt;
+      need_eq[row] = need;
       row_max[(int64_t)h * nb + i] = m;
     }
   }
