@@ -244,3 +244,82 @@ def dequant(x: torch.Tensor, scale: float = 1.0) -> torch.Tensor:
     if x.dtype == torch.float8_e4m3fn:
         return x.float() * scale
     return x.float()
+
+
+@dataclass
+class Batch:
+    """A packed batch of independent sequences (varlen), optionally with K/V
+    in a paged cache.  Data layout only; no method arithmetic."""
+
+    cfg: LayerConfig
+    seq_lens: Sequence[int]
+    cu_seqlens: Sequence[int]  # [S + 1] token offsets into q / out (and k / v when packed)
+    q32: torch.Tensor  # [T, Hq, d] fp32, exactly the values the kernels see
+    k32: torch.Tensor  # [T, Hkv, d]
+    v32: torch.Tensor
+    q: torch.Tensor  # kernel inputs, packed
+    k: torch.Tensor
+    v: torch.Tensor
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    # paged K/V: cache [num_pages, B, Hkv, d] in the kernel dtype (pages past a
+    # sequence's end are zero) and block_table [S, max_blocks] of page ids
+    # (-1 where a sequence has no block)
+    k_cache: Optional[torch.Tensor] = None
+    v_cache: Optional[torch.Tensor] = None
+    block_table: Optional[torch.Tensor] = None
+
+
+def make_batch(cfg: LayerConfig, seq_lens: Sequence[int], device="cpu", seed: Optional[int] = None,
+               paged: bool = False, spare_pages: int = 3) -> Batch:
+    """Sequences of the given lengths, each built like ``make_layer`` with its
+    own seed (seed + 1000 s), concatenated token-major and cast once (one
+    per-tensor fp8 scale for the batch).  With ``paged``, K and V also go to a
+    cache of block_size-token pages in a seeded random order, with
+    ``spare_pages`` unused pages mixed in."""
+    seed = cfg.seed if seed is None else seed
+    parts = []
+    for s, L in enumerate(seq_lens):
+        c = replace(cfg, seq_len=int(L))
+        qs, ks, vs, _ = _build_fp32(c, seed + 1000 * s, device)
+        parts.append((qs, ks, vs))
+    q = torch.cat([p[0] for p in parts])
+    k = torch.cat([p[1] for p in parts])
+    v = torch.cat([p[2] for p in parts])
+    del parts
+    cu = [0]
+    for L in seq_lens:
+        cu.append(cu[-1] + int(L))
+    if cfg.dtype == "f32":
+        b = Batch(cfg, list(seq_lens), cu, q, k, v, q, k, v)
+    elif cfg.dtype == "bf16":
+        qb, kb, vb = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+        b = Batch(cfg, list(seq_lens), cu, qb.float(), kb.float(), vb.float(), qb, kb, vb)
+    elif cfg.dtype == "fp8":
+        (qq, sq), (kq, sk), (vq, sv) = _fp8_quant(q), _fp8_quant(k), _fp8_quant(v)
+        b = Batch(cfg, list(seq_lens), cu, qq.float() * sq, kq.float() * sk, vq.float() * sv,
+                  qq, kq, vq, sq, sk, sv)
+    else:
+        raise ValueError(f"unknown dtype {cfg.dtype}")
+    if paged:
+        B = cfg.block_size
+        nbs = [(L + B - 1) // B for L in seq_lens]
+        n_pages = sum(nbs) + spare_pages
+        gen = torch.Generator(device="cpu").manual_seed(seed + 7)
+        perm = torch.randperm(n_pages, generator=gen).tolist()
+        Hkv, d = cfg.num_kv_heads, cfg.head_dim
+        kc = torch.zeros((n_pages, B, Hkv, d), dtype=b.k.dtype, device=device)
+        vc = torch.zeros((n_pages, B, Hkv, d), dtype=b.v.dtype, device=device)
+        table = torch.full((len(seq_lens), max(max(nbs), 1)), -1, dtype=torch.int32)
+        nxt = 0
+        for s, L in enumerate(seq_lens):
+            for j in range(nbs[s]):
+                pg = perm[nxt]
+                nxt += 1
+                t0, t1 = cu[s] + j * B, min(cu[s] + (j + 1) * B, cu[s + 1])
+                kc[pg, : t1 - t0] = b.k[t0:t1]
+                vc[pg, : t1 - t0] = b.v[t0:t1]
+                table[s, j] = pg
+        b.k_cache, b.v_cache, b.block_table = kc, vc, table.to(device)
+    return b
