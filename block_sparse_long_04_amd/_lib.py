@@ -23,7 +23,8 @@ FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP = 0, -1,
 FP_SELECT_TOPK, FP_SELECT_TOPP = 1, 2
 
 EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_sorted",
-            "fp_sparse_prefill", "fp_strerror")
+            "fp_sparse_prefill", "fp_workspace_layout_varlen", "fp_block_pool_varlen",
+            "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_strerror")
 
 
 class FpProblem(ctypes.Structure):
@@ -42,6 +43,18 @@ class FpProblem(ctypes.Structure):
         ("sm_scale", ctypes.c_float), ("threshold", ctypes.c_float),
         ("causal", ctypes.c_int32),
     ]
+
+
+class FpVarlen(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
+                ("cu_seqlens_dev", ctypes.c_void_p), ("block_table_dev", ctypes.c_void_p),
+                ("max_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("k_page_stride", ctypes.c_int64), ("v_page_stride", ctypes.c_int64)]
+
+
+class FpWsLayoutVarlen(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("q_pool", "k_pool", "row_max", "counts", "indices", "v_t", "k_c", "meta", "total")]
 
 
 class FpWsLayout(ctypes.Structure):
@@ -77,6 +90,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_block_select_sorted.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p]
     lib.fp_block_select_sorted.restype = ctypes.c_int
+    VL = ctypes.POINTER(FpVarlen)
+    lib.fp_workspace_layout_varlen.argtypes = [P, VL, ctypes.POINTER(FpWsLayoutVarlen)]
+    lib.fp_workspace_layout_varlen.restype = ctypes.c_int
+    for name in ("fp_block_pool_varlen", "fp_block_select_varlen", "fp_sparse_prefill_varlen"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, VL, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
     lib.fp_strerror.argtypes = [ctypes.c_int]
     lib.fp_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -122,6 +142,28 @@ def fp_block_select_sorted(prob: FpProblem, rule: int, param: float, ws_ptr: int
 def fp_sparse_prefill(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check(load_library().fp_sparse_prefill(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
            "fp_sparse_prefill")
+
+
+def fp_workspace_layout_varlen(prob: FpProblem, vl: FpVarlen) -> FpWsLayoutVarlen:
+    lay = FpWsLayoutVarlen()
+    _check(load_library().fp_workspace_layout_varlen(ctypes.byref(prob), ctypes.byref(vl), ctypes.byref(lay)),
+           "fp_workspace_layout_varlen")
+    return lay
+
+
+def fp_block_pool_varlen(prob, vl, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_block_pool_varlen(ctypes.byref(prob), ctypes.byref(vl), ws_ptr, ws_bytes, stream),
+           "fp_block_pool_varlen")
+
+
+def fp_block_select_varlen(prob, vl, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_block_select_varlen(ctypes.byref(prob), ctypes.byref(vl), ws_ptr, ws_bytes, stream),
+           "fp_block_select_varlen")
+
+
+def fp_sparse_prefill_varlen(prob, vl, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_sparse_prefill_varlen(ctypes.byref(prob), ctypes.byref(vl), ws_ptr, ws_bytes,
+                                                   stream), "fp_sparse_prefill_varlen")
 
 
 # ----------------------------------------------------------------------------
@@ -290,3 +332,113 @@ def prefill(q, k, v, threshold: float = 0.1, block_size: int = 128, **kw):
 
 def default_sm_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+class PrefillVarlen:
+    """A batch of sequences (varlen): q / out packed [T, Hq, d]; k / v packed
+    [T, Hkv, d], or page caches [pages, B, Hkv, d] with a block table
+    [S, max_blocks] of page ids.  cu_seqlens: S + 1 token offsets (host list).
+    Same pool / select / attend steps as Prefill, over every sequence."""
+
+    def __init__(self, q, k, v, cu_seqlens, block_size: int = 128, threshold: float = 0.1,
+                 sm_scale: float = 0.0, q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0,
+                 block_table=None, out=None):
+        import torch
+        if not (q.is_cuda and k.is_cuda and v.is_cuda):
+            raise ValueError("q/k/v must be device tensors")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        self.q, self.k, self.v, self.out = q, k, v, out
+        T, Hq, d = q.shape
+        Hkv = k.shape[-2]
+        self.prob = make_problem(q, None, None, out, block_size, threshold, sm_scale, q_scale, k_scale,
+                                 v_scale, seq_len=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d)
+        self.prob.k, self.prob.v = k.data_ptr(), v.data_ptr()
+        paged = block_table is not None
+        # inside a page (or the packed tensor) token / head strides
+        self.prob.k_stride_tok, self.prob.k_stride_head = k.stride(-3), k.stride(-2)
+        self.prob.v_stride_tok, self.prob.v_stride_head = v.stride(-3), v.stride(-2)
+        self.cu_host = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+        self.cu_dev = torch.tensor([int(x) for x in cu_seqlens], dtype=torch.int32, device=q.device)
+        vl = FpVarlen()
+        vl.num_seqs = len(cu_seqlens) - 1
+        vl.cu_seqlens = self.cu_host
+        vl.cu_seqlens_dev = self.cu_dev.data_ptr()
+        if paged:
+            self.table = block_table.to(device=q.device, dtype=torch.int32).contiguous()
+            vl.block_table_dev = self.table.data_ptr()
+            vl.max_blocks = self.table.shape[1]
+            vl.num_pages = k.shape[0]
+            vl.k_page_stride, vl.v_page_stride = k.stride(0), v.stride(0)
+        else:
+            vl.block_table_dev = None
+        self.vl = vl
+        self.layout = fp_workspace_layout_varlen(self.prob, vl)
+        self.buf = torch.empty(max(int(self.layout.total), 256), dtype=torch.uint8, device=q.device)
+        B = block_size
+        self.nbs = [(int(cu_seqlens[s + 1]) - int(cu_seqlens[s]) + B - 1) // B for s in range(vl.num_seqs)]
+        self.NB = sum(self.nbs)
+        self.Hq, self.Hkv, self.d = Hq, Hkv, d
+        self.device = q.device
+
+    def stream(self) -> int:
+        return current_stream(self.device)
+
+    def pool(self):
+        fp_block_pool_varlen(self.prob, self.vl, self.buf.data_ptr(), self.buf.numel(), self.stream())
+
+    def select(self):
+        fp_block_select_varlen(self.prob, self.vl, self.buf.data_ptr(), self.buf.numel(), self.stream())
+
+    def attend(self):
+        fp_sparse_prefill_varlen(self.prob, self.vl, self.buf.data_ptr(), self.buf.numel(), self.stream())
+
+    def run(self):
+        self.pool()
+        self.select()
+        self.attend()
+        return self.out
+
+    def _view(self, off, count, dtype):
+        import torch
+        esz = torch.empty((), dtype=dtype).element_size()
+        return self.buf[off: off + count * esz].view(dtype)
+
+    def counts(self):
+        import torch
+        return self._view(self.layout.counts, self.Hq * self.NB, torch.int32).view(self.Hq, self.NB)
+
+    def row_max(self):
+        import torch
+        return self._view(self.layout.row_max, self.Hq * self.NB, torch.float32).view(self.Hq, self.NB)
+
+    def q_pool(self):
+        import torch
+        return self._view(self.layout.q_pool, self.Hq * self.NB * self.d, torch.float32).view(
+            self.Hq, self.NB, self.d)
+
+    def k_pool(self):
+        import torch
+        return self._view(self.layout.k_pool, self.Hkv * self.NB * self.d, torch.float32).view(
+            self.Hkv, self.NB, self.d)
+
+    def lists(self):
+        """Host lists [s][h][i] (local block indices) from the workspace."""
+        import numpy as np
+        counts = self.counts().cpu().numpy()
+        total = sum(self.Hq * n * (n + 1) // 2 for n in self.nbs)
+        idx = self._view(self.layout.indices, total, __import__("torch").int32).cpu().numpy()
+        res, base, first = [], 0, 0
+        for n in self.nbs:
+            tri = n * (n + 1) // 2
+            per_h = []
+            for h in range(self.Hq):
+                rows = []
+                for i in range(n):
+                    off = base + h * tri + i * (i + 1) // 2
+                    rows.append(idx[off: off + int(counts[h, first + i])].astype(np.int32))
+                per_h.append(rows)
+            res.append(per_h)
+            base += self.Hq * tri
+            first += n
+        return res

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "varlen.h"
 
 namespace {
 
@@ -109,6 +110,75 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
 }
 
+
+// ---- batches (varlen) ------------------------------------------------------
+
+struct VlInfo {
+  int NB;             // blocks of the batch
+  int64_t idx_total;  // int32 entries of all index lists
+};
+
+// Checks of *vl against *p (host side: cu_seqlens is read here).
+int check_varlen(const fp_problem* p, const fp_varlen* vl, const FpDims& dm, VlInfo* vi) {
+  if (!vl || vl->num_seqs < 1 || !vl->cu_seqlens) return FP_ERR_INVALID;
+  if (p->dtype == FP_F32 || dm.d != 128 || dm.B != 128) return FP_ERR_UNSUPPORTED;
+  const int32_t* cu = vl->cu_seqlens;
+  if (cu[0] != 0 || cu[vl->num_seqs] != p->seq_len) return FP_ERR_INVALID;
+  int64_t nb_all = 0, tri = 0, nb_max = 0;
+  for (int s = 0; s < vl->num_seqs; ++s) {
+    if (cu[s + 1] < cu[s]) return FP_ERR_INVALID;
+    const int64_t nbs = ((int64_t)cu[s + 1] - cu[s] + dm.B - 1) / dm.B;
+    nb_all += nbs;
+    tri += nbs * (nbs + 1) / 2;
+    nb_max = nbs > nb_max ? nbs : nb_max;
+  }
+  if (nb_all > kMaxBlocks) return FP_ERR_UNSUPPORTED;
+  if (vl->block_table_dev) {
+    const int es = elem_size(p->dtype);
+    if (vl->max_blocks < nb_max || vl->num_pages < 1 || vl->k_page_stride <= 0 || vl->v_page_stride <= 0 ||
+        (vl->k_page_stride * es) % 16 != 0 || (vl->v_page_stride * es) % 16 != 0)
+      return FP_ERR_INVALID;
+  }
+  vi->NB = (int)nb_all;
+  vi->idx_total = tri * dm.Hq;
+  return FP_OK;
+}
+
+void layout_varlen(const fp_problem* p, const FpDims& dm, const VlInfo& vi, int S, fp_ws_layout_varlen* w) {
+  const size_t NB = (size_t)vi.NB;
+  size_t off = 0;
+  w->q_pool = off;
+  off = align_up(off + (size_t)dm.Hq * NB * dm.d * sizeof(float));
+  w->k_pool = off;
+  off = align_up(off + (size_t)dm.Hkv * NB * dm.d * sizeof(float));
+  w->row_max = off;
+  off = align_up(off + (size_t)dm.Hq * NB * sizeof(float));
+  w->counts = off;
+  off = align_up(off + (size_t)dm.Hq * NB * sizeof(int));
+  w->indices = off;
+  off = align_up(off + (size_t)vi.idx_total * sizeof(int));
+  w->v_t = off;
+  off = align_up(off + (size_t)dm.Hkv * dm.d * NB * dm.B * sizeof(uint16_t));
+  w->k_c = off;
+  off = align_up(off + (size_t)dm.Hkv * NB * dm.B * dm.d * elem_size(p->dtype));
+  w->meta = off;
+  off = align_up(off + NB * sizeof(fpk::VlBlock) + (size_t)S * sizeof(fpk::VlSeq));
+  w->total = NB == 0 ? 0 : off;
+}
+
+int check_ws_varlen(const fp_problem* p, const fp_varlen* vl, FpDims* dm, VlInfo* vi, void* ws, size_t bytes,
+                    fp_ws_layout_varlen* w) {
+  int rc = check_problem(p, dm);
+  if (rc != FP_OK) return rc;
+  rc = check_varlen(p, vl, *dm, vi);
+  if (rc != FP_OK) return rc;
+  layout_varlen(p, *dm, *vi, vl->num_seqs, w);
+  if (vi->NB == 0) return FP_OK;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 || bytes < w->total)
+    return FP_ERR_WORKSPACE;
+  return FP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +271,71 @@ int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_byt
   } else {
     e = fpk_launch_attn_generic(*p, dm, counts, indices, sc, st);
   }
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_workspace_layout_varlen(const fp_problem* p, const fp_varlen* vl, fp_ws_layout_varlen* layout) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  VlInfo vi;
+  rc = check_varlen(p, vl, dm, &vi);
+  if (rc != FP_OK) return rc;
+  if (!layout) return FP_ERR_INVALID;
+  layout_varlen(p, dm, vi, vl->num_seqs, layout);
+  return FP_OK;
+}
+
+int fp_block_pool_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  FpDims dm;
+  VlInfo vi;
+  fp_ws_layout_varlen w;
+  int rc = check_ws_varlen(p, vl, &dm, &vi, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  if (vi.NB == 0) return FP_OK;
+  if (!p->q || !p->k || !p->v || !aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) ||
+      !vl->cu_seqlens_dev)
+    return FP_ERR_INVALID;
+  const hipError_t e = fpk_launch_varlen_prepare(
+      *p, *vl, dm, vi.NB, at<fpk::VlBlock>(workspace, w.meta),
+      reinterpret_cast<fpk::VlSeq*>(at<fpk::VlBlock>(workspace, w.meta) + vi.NB), at<float>(workspace, w.q_pool),
+      at<float>(workspace, w.k_pool), at<uint8_t>(workspace, w.k_c), at<uint16_t>(workspace, w.v_t),
+      (hipStream_t)stream);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_block_select_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  FpDims dm;
+  VlInfo vi;
+  fp_ws_layout_varlen w;
+  int rc = check_ws_varlen(p, vl, &dm, &vi, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  if (vi.NB == 0) return FP_OK;
+  const float lt = p->threshold == 0.f ? -INFINITY : (float)log((double)p->threshold);
+  const fpk::VlBlock* blk = at<fpk::VlBlock>(workspace, w.meta);
+  const hipError_t e = fpk_launch_select_varlen(
+      dm, vi.NB, blk, reinterpret_cast<const fpk::VlSeq*>(blk + vi.NB), at<float>(workspace, w.q_pool),
+      at<float>(workspace, w.k_pool), eff_sm_scale(p), lt, at<float>(workspace, w.row_max),
+      at<int>(workspace, w.counts), at<int>(workspace, w.indices), (hipStream_t)stream);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_sparse_prefill_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  FpDims dm;
+  VlInfo vi;
+  fp_ws_layout_varlen w;
+  int rc = check_ws_varlen(p, vl, &dm, &vi, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  if (vi.NB == 0) return FP_OK;
+  if (!p->q || !p->out || !aligned16(p->q) || !aligned16(p->out)) return FP_ERR_INVALID;
+  const fpk::VlBlock* blk = at<fpk::VlBlock>(workspace, w.meta);
+  const hipError_t e = fpk_launch_attn_mfma_varlen(
+      *p, dm, vi.NB, blk, reinterpret_cast<const fpk::VlSeq*>(blk + vi.NB), at<int>(workspace, w.counts),
+      at<int>(workspace, w.indices), at<uint8_t>(workspace, w.k_c), at<uint16_t>(workspace, w.v_t),
+      eff_sm_scale(p), (hipStream_t)stream);
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 

@@ -45,6 +45,7 @@
 // Work order: heavy (late) query blocks first, and the workgroups one XCD
 // runs together belong to one kv group (work_item below).
 #include "common.h"
+#include "varlen.h"
 
 namespace {
 
@@ -59,6 +60,8 @@ struct AttnArgs {
   uint16_t* out;
   const int* counts;
   const int* indices;
+  const fpk::VlBlock* blk;  // batch metadata (varlen kernel only)
+  const fpk::VlSeq* seq;
   int64_t q_st, q_sh, k_st, k_sh, o_st, o_sh;
   int L, Hq, Hkv, nb, Lpad;
   float scale_log2;  // sm_scale * log2(e) (times q_scale * k_scale for e4m3 inputs)
@@ -502,7 +505,7 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kVarlen>
 __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 waves per SIMD: two workgroups per CU
   // K unit m lives in sK[m & 1], V^T unit m in sV[m & 1]; K runs one unit
   // ahead of V because S(n+1) = K(n+1) Q^T is issued before P(n) V(n).
@@ -520,12 +523,27 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // = query group
   const int qi = lane & 31;
   const int hh = lane >> 5;
-  const int tq = i * 128 + 32 * w + qi;
+  // Tokens of block i in q / out, and its list.  One sequence: block i is
+  // tokens 128 i .. and row (h, i) of the triangle.  A batch (varlen): block
+  // i of the batch is block li of its sequence, which starts at block
+  // `first`; list entries are local to the sequence.
+  int tok0 = i * 128, rows = min(128, a.L - i * 128), li = i, first = 0;
+  const int* lst = a.indices + fpk::tri_offset(h, i, a.nb);
+  if constexpr (kVarlen) {
+    const fpk::VlBlock m = a.blk[i];
+    const fpk::VlSeq sq = a.seq[m.seq];
+    tok0 = m.tok0;
+    rows = m.rows;
+    li = m.jl;
+    first = sq.first;
+    lst = a.indices + sq.idx_base + (int64_t)h * sq.nb * (sq.nb + 1) / 2 + (int64_t)li * (li + 1) / 2;
+  }
+  const int tq = tok0 + 32 * w + qi;
+  const bool q_valid = 32 * w + qi < rows;
   const int pm = (qi & 0x13) | ((qi & 4) << 1) | ((qi & 8) >> 1);
   const float c = a.scale_log2;
 
   const int cnt = a.counts[(int64_t)h * a.nb + i];
-  const int* lst = a.indices + fpk::tri_offset(h, i, a.nb);
 
   // The kept list is read 64 entries at a time into one VGPR (lane e holds
   // entry base + e) and entries are taken with readlane: no per-unit memory
@@ -535,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
   // wait for the count: both loads are in flight together.  Entries at or
   // past the count are never selected.
   const __amdgpu_buffer_rsrc_t lrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(lst), 0, (i + 1) * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(lst), 0, (li + 1) * 4, 0x00020000);
   int win = (int)__builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, 0, 0);
   int wbase = 0;
   auto entry = [&](int n) -> int {
@@ -544,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
       win = (int)__builtin_amdgcn_raw_buffer_load_b32(lrs, (wbase + lane) * 4, 0, 0);
       FP_WAIT_VMEM();
     }
-    return __builtin_amdgcn_readlane(win, n - wbase);
+    return __builtin_amdgcn_readlane(win, n - wbase) + first;
   };
 
   TileLoader<kFp8> ld;
@@ -553,7 +571,7 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
   // B operand of S^T = K Q^T for query row tq
   QFrag<kFp8> qf;
   if constexpr (!kFp8) {
-    if (tq < a.L) {
+    if (q_valid) {
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)tq * a.q_st +
                            (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
@@ -565,7 +583,7 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
   } else {
 #pragma unroll
     for (int s = 0; s < 2; ++s) qf.f[s] = (intx8){0, 0, 0, 0, 0, 0, 0, 0};
-    if (tq < a.L) {
+    if (q_valid) {
       const uint8_t* qp = a.q + (int64_t)tq * a.q_st + (int64_t)h * a.q_sh + 32 * hh;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -691,11 +709,18 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(AttnArgs a) {  // 2 w
     const int ch = it * 64 + lane;  // 16-byte chunk: token ch / 16, piece ch % 16
     const int tok = ch >> 4;
     const uint4 v = *reinterpret_cast<const uint4*>(stg + tok * kStageRow + (ch & 15) * 16);
-    const int t = i * 128 + 32 * w + tok;
-    if (t < a.L)
+    const int t = tok0 + 32 * w + tok;
+    if (32 * w + tok < rows)
       *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + (ch & 15) * 8) = v;
   }
 }
+
+// Explicit instantiations: the launchers below name these variants from
+// outside the unnamed namespace.
+template __global__ void attn_d128_kernel<false, false>(AttnArgs);
+template __global__ void attn_d128_kernel<true, false>(AttnArgs);
+template __global__ void attn_d128_kernel<false, true>(AttnArgs);
+template __global__ void attn_d128_kernel<true, true>(AttnArgs);
 
 }  // namespace
 
@@ -725,8 +750,45 @@ hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int
   a.out_scale = fp8 ? p.v_scale : 1.0f;
   const dim3 grid((unsigned)(dm.nb * dm.Hq));
   if (fp8)
-    hipLaunchKernelGGL(attn_d128_kernel<true>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_d128_kernel<true, false>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_d128_kernel<false>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_d128_kernel<false, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t fpk_launch_attn_mfma_varlen(const fp_problem& p, const FpDims& dm, int NB, const fpk::VlBlock* blk,
+                                       const fpk::VlSeq* seq, const int* counts, const int* indices,
+                                       const uint8_t* k_c, const uint16_t* v_t, float sm_scale, hipStream_t st) {
+  // K is read from the gathered copy [Hkv][NB * 128][128]: full blocks, rows
+  // past a sequence's end zero (the causal mask of the diagonal block hides
+  // them), so the loader never takes its ragged path.
+  AttnArgs a{};
+  a.q = static_cast<const uint8_t*>(p.q);
+  a.k = k_c;
+  a.vt = v_t;
+  a.out = static_cast<uint16_t*>(p.out);
+  a.counts = counts;
+  a.indices = indices;
+  a.blk = blk;
+  a.seq = seq;
+  a.q_st = p.q_stride_tok;
+  a.q_sh = p.q_stride_head;
+  a.k_st = 128;
+  a.k_sh = (int64_t)NB * 128 * 128;
+  a.o_st = p.o_stride_tok;
+  a.o_sh = p.o_stride_head;
+  a.L = NB * 128;
+  a.Hq = dm.Hq;
+  a.Hkv = dm.Hkv;
+  a.nb = NB;
+  a.Lpad = NB * 128;
+  const bool fp8 = p.dtype == FP_FP8_E4M3;
+  a.scale_log2 = sm_scale * (fp8 ? p.q_scale * p.k_scale : 1.0f) * 1.4426950408889634f;
+  a.out_scale = fp8 ? p.v_scale : 1.0f;
+  const dim3 grid((unsigned)(NB * dm.Hq));
+  if (fp8)
+    hipLaunchKernelGGL((attn_d128_kernel<true, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_d128_kernel<false, true>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

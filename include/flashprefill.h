@@ -144,6 +144,66 @@ int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* wor
  * indices; writes out.  Must follow fp_block_pool on the same workspace. */
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Batches of independent sequences (varlen), K/V packed or paged.
+ *
+ * FlashPrefill V2 abstract: the method serves many prompts prefilled together
+ * with K/V in a paged cache.  Each sequence is its own causal prefill (the
+ * steps above on its own tokens and blocks); only where the tokens live
+ * changes.  p->seq_len is the total token count T of q / out, which are packed
+ * token-major: sequence s owns rows cu_seqlens[s] .. cu_seqlens[s+1]-1.  k / v
+ * are packed the same way when block_table_dev is NULL; otherwise p->k / p->v
+ * point at page caches whose page of block_size tokens starts every
+ * k_page_stride / v_page_stride elements, token r of a page at
+ * r * k_stride_tok + head * k_stride_head inside it, and block j of sequence s
+ * is page block_table_dev[s * max_blocks + j] (ids outside [0, num_pages) read
+ * as zero pages).  Supported for bf16 and e4m3 inputs with head_dim 128 and
+ * block_size 128 (FP_ERR_UNSUPPORTED otherwise); at most 16384 blocks in all.
+ * --------------------------------------------------------------------------- */
+typedef struct fp_varlen {
+  int32_t num_seqs;                /* S >= 1 */
+  const int32_t* cu_seqlens;       /* host [S + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[S] = p->seq_len */
+  const int32_t* cu_seqlens_dev;   /* the same S + 1 values in device memory */
+  const int32_t* block_table_dev;  /* NULL (packed k / v) or device [S][max_blocks] page ids */
+  int32_t max_blocks;              /* row stride of the block table (>= every sequence's block count) */
+  int32_t num_pages;               /* pages in each cache */
+  int64_t k_page_stride, v_page_stride;  /* elements between pages */
+} fp_varlen;
+
+/* Workspace of a batch, NB = sum over s of ceil(len_s / block_size) blocks.
+ *   q_pool, k_pool, row_max, counts, v_t: as for one sequence over the NB
+ *           blocks of the batch in order (sequence s's blocks first[s] ..
+ *           first[s] + nb[s] - 1, first[s] = sum of the earlier nb);
+ *   indices: sequence s's lists start at idx_base[s] = num_q_heads * (sum of
+ *           nb[s'] (nb[s'] + 1) / 2 over s' < s); within it row (h, i) at
+ *           h * nb[s] (nb[s] + 1) / 2 + i * (i + 1) / 2; entries are block
+ *           indices local to the sequence (0 = its first block);
+ *   k_c     K gathered per kv head [num_kv_heads][NB * block_size][head_dim]
+ *           (input dtype, zero past each sequence's end);
+ *   meta    per block int32 x4 (sequence, block in sequence, first token in q / out,
+ *           rows), then per sequence int32 first, int32 nb, int64 idx_base. */
+typedef struct fp_ws_layout_varlen {
+  size_t q_pool, k_pool, row_max, counts, indices, v_t, k_c, meta, total;
+} fp_ws_layout_varlen;
+
+/* Host only: validates *p and *vl (vl->cu_seqlens is read; device pointers
+ * may be NULL here) and fills *layout. */
+int fp_workspace_layout_varlen(const fp_problem* p, const fp_varlen* vl, fp_ws_layout_varlen* layout);
+
+/* Step 1 of every sequence: block metadata, pooled proxies, gathered K and
+ * V^T (reads q, k, v and cu_seqlens_dev / block_table_dev). */
+int fp_block_pool_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Steps 2-4 of every sequence (rows see only their own sequence's blocks). */
+int fp_block_select_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Step 5 of every sequence; writes out.  Must follow fp_block_pool_varlen on
+ * the same workspace. */
+int fp_sparse_prefill_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Static, human-readable text of a return code. */
 const char* fp_strerror(int code);
 

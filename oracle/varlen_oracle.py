@@ -64,6 +64,9 @@ def prefill_varlen(q: np.ndarray, k: Optional[np.ndarray], v: Optional[np.ndarra
     seqs = []
     for s in range(S):
         c0, c1 = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        if c1 == c0:  # an empty sequence has no blocks and no output rows
+            seqs.append(dict(lists=[], empty=True))
+            continue
         ks, vs = sequence_kv(k, v, cu_seqlens, s, block_size, k_cache, v_cache, table)
         r = O.prefill(q[c0:c1], ks, vs, block_size, tau, sm_scale, attention=attention)
         r["k"], r["v"] = ks, vs

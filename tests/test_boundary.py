@@ -38,7 +38,9 @@ def test_struct_layout_matches_header(tmp_path):
         pytest.skip("no C compiler")
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "flashprefill.h"',
              'int main(void) {']
-    for struct, cls in (("fp_problem", fp.FpProblem), ("fp_ws_layout", fp.FpWsLayout)):
+    structs = (("fp_problem", fp.FpProblem), ("fp_ws_layout", fp.FpWsLayout), ("fp_varlen", fp.FpVarlen),
+               ("fp_ws_layout_varlen", fp.FpWsLayoutVarlen))
+    for struct, cls in structs:
         lines.append(f'printf("{struct} %zu\\n", sizeof({struct}));')
         for name, _ in cls._fields_:
             lines.append(f'printf("{struct}.{name} %zu\\n", offsetof({struct}, {name}));')
@@ -49,7 +51,7 @@ def test_struct_layout_matches_header(tmp_path):
     subprocess.run([cc, "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
     got = dict(ln.split() for ln in subprocess.run([str(exe)], capture_output=True, text=True,
                                                     check=True).stdout.splitlines())
-    for struct, cls in (("fp_problem", fp.FpProblem), ("fp_ws_layout", fp.FpWsLayout)):
+    for struct, cls in structs:
         assert int(got[struct]) == ctypes.sizeof(cls)
         for name, _ in cls._fields_:
             assert int(got[f"{struct}.{name}"]) == getattr(cls, name).offset, name
@@ -179,3 +181,68 @@ def test_sorted_selection_rejects_bad_rules_and_sizes_before_launch():
     assert e.value.code == fp.FP_ERR_UNSUPPORTED
     # empty problem: nothing launched
     fp.fp_block_select_sorted(prob(seq_len=0), fp.FP_SELECT_TOPK, 1.0, 0, 0, 0)
+
+
+def _varlen(lens, table=False, max_blocks=0, num_pages=0, kps=0, vps=0):
+    vl = fp.FpVarlen()
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    vl.num_seqs = len(lens)
+    vl.cu_seqlens = arr
+    vl.cu_seqlens_dev = 1 << 20
+    vl.block_table_dev = (1 << 21) if table else None
+    vl.max_blocks, vl.num_pages, vl.k_page_stride, vl.v_page_stride = max_blocks, num_pages, kps, vps
+    return vl, arr, cu[-1]
+
+
+def test_varlen_layout_and_host_validation():
+    lens = [300, 129, 0, 1000]
+    vl, arr, T = _varlen(lens)
+    p = prob(seq_len=T)
+    lay = fp.fp_workspace_layout_varlen(p, vl)
+    nbs = [(L + 127) // 128 for L in lens]
+    NB = sum(nbs)
+    offs = [lay.q_pool, lay.k_pool, lay.row_max, lay.counts, lay.indices, lay.v_t, lay.k_c, lay.meta, lay.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.k_pool - lay.q_pool >= 8 * NB * 128 * 4
+    assert lay.v_t - lay.indices >= 8 * sum(n * (n + 1) // 2 for n in nbs) * 4
+    assert lay.k_c - lay.v_t >= 2 * 128 * NB * 128 * 2
+    assert lay.meta - lay.k_c >= 2 * NB * 128 * 128 * 2
+    assert lay.total - lay.meta >= NB * 16 + len(lens) * 16
+    fake = 1 << 22
+    p.q, p.k, p.v, p.out = fake, fake, fake, fake
+    # cu_seqlens must start at 0, end at seq_len and not decrease
+    for bad in ([0, 300, 200, 1429], [1, 300, 429, 1429], [0, 300, 429, 1428]):
+        a = (ctypes.c_int32 * len(bad))(*bad)
+        v2, _, _ = _varlen([1])
+        v2.num_seqs, v2.cu_seqlens = len(bad) - 1, a
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fp.fp_workspace_layout_varlen(prob(seq_len=1429), v2)
+        assert e.value.code == fp.FP_ERR_INVALID
+    # only the matrix-core shapes
+    for kw in (dict(dtype=fp.FP_F32), dict(head_dim=64), dict(block_size=64)):
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fp.fp_workspace_layout_varlen(prob(seq_len=T, **kw), vl)
+        assert e.value.code == fp.FP_ERR_UNSUPPORTED
+    # paged: the block table must cover every sequence, strides must be aligned
+    vp, _, _ = _varlen(lens, table=True, max_blocks=7, num_pages=20, kps=128 * 2 * 128, vps=128 * 2 * 128)
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_workspace_layout_varlen(p, vp)
+    assert e.value.code == fp.FP_ERR_INVALID
+    vp.max_blocks = 8
+    fp.fp_workspace_layout_varlen(p, vp)
+    vp.k_page_stride = 3
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_workspace_layout_varlen(p, vp)
+    assert e.value.code == fp.FP_ERR_INVALID
+    # workspace checks before any launch
+    for fn in (fp.fp_block_pool_varlen, fp.fp_block_select_varlen, fp.fp_sparse_prefill_varlen):
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fn(p, vl, fake, lay.total - 1, 0)
+        assert e.value.code == fp.FP_ERR_WORKSPACE
+    # an empty batch is a no-op
+    ve, _, _ = _varlen([0, 0])
+    for fn in (fp.fp_block_pool_varlen, fp.fp_block_select_varlen, fp.fp_sparse_prefill_varlen):
+        fn(prob(seq_len=0), ve, 0, 0, 0)
