@@ -11,8 +11,10 @@ bf16, tau = 0.1).
 Prints ONE JSON line: value = kept-block TFLOP/s over the whole step
 (algorithmic FLOPs of the kept (query, key) pairs / ms per layer), plus
 per-stage times, the attention kernel's roofline, the CPU oracle timed on a
-bounded sample of the same layer on this host, and (up to 2048 blocks) the
-sorting / cumulative-sum selection baselines timed next to the threshold.
+bounded sample of the same layer on this host, (up to 2048 blocks) the
+sorting / cumulative-sum selection baselines timed next to the threshold, and
+(for the default workload) a serving-like batch of sequences with K/V in a
+paged cache, run as one batch and one sequence at a time.
 """
 from __future__ import annotations
 
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the batch (varlen, paged K/V) measurement of the default workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -232,6 +236,53 @@ def select_baselines(pf, _lib, torch, thr_ms, k, p, reps=5):
     return out
 
 
+# a serving-like mix of prompts: 4 of about 8K, 8 of 4K, 16 of 2K, 32 of 1K
+# tokens (ragged lengths), 128K tokens in all
+VARLEN_LENS = tuple([8192 - 37 * k for k in range(4)] + [4096 - 29 * k for k in range(8)] +
+                    [2048 - 13 * k for k in range(16)] + [1024 - 7 * k for k in range(32)])
+
+
+def varlen_batch(cfg, _lib, make_batch, kept_pairs, torch, np, reps=5):
+    """A serving-like batch (VARLEN_LENS, K/V in a paged cache) through the
+    fp_*_varlen calls, against the same sequences run one at a time through the
+    single-sequence calls.  Median of `reps` whole runs each."""
+    dev = torch.device("cuda:0")
+    b = make_batch(cfg, VARLEN_LENS, device=dev, paged=True)
+    tau = cfg.taus[0]
+    pv = _lib.PrefillVarlen(b.q, b.k_cache, b.v_cache, b.cu_seqlens, block_size=cfg.block_size,
+                            threshold=tau, block_table=b.block_table)
+    singles = []
+    for s in range(len(VARLEN_LENS)):
+        c0, c1 = b.cu_seqlens[s], b.cu_seqlens[s + 1]
+        singles.append(_lib.Prefill(b.q[c0:c1].contiguous(), b.k[c0:c1].contiguous(),
+                                    b.v[c0:c1].contiguous(), block_size=cfg.block_size, threshold=tau))
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[reps // 2]
+
+    ms_batch = timed(pv.run)
+    ms_single = timed(lambda: [x.run() for x in singles])
+    counts = pv.counts().cpu().numpy()
+    pairs, first = 0, 0
+    for L in VARLEN_LENS:
+        nb = (L + cfg.block_size - 1) // cfg.block_size
+        pairs += kept_pairs(counts[:, first:first + nb], L, cfg.block_size)
+        first += nb
+    flops = 4.0 * cfg.head_dim * pairs
+    return {"seq_lens": list(VARLEN_LENS), "tokens": int(b.cu_seqlens[-1]), "paged_kv": True,
+            "ms_batch": round(ms_batch, 4), "ms_one_by_one": round(ms_single, 4),
+            "kept_tflops_batch": round(flops / (ms_batch * 1e-3) / 1e12, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -356,6 +407,12 @@ def main():
         k_match = max(1, int(round(float(counts.mean()))))
         res["select_baselines"] = select_baselines(pf, _lib, torch, stage_ms["select"], k_match, 0.9)
         pf.select()  # leave the threshold's lists in the workspace
+    if not args.no_varlen and args.config == "c4":
+        # a batch of sequences with K/V in pages, totalling about the same tokens
+        print("[bench] varlen batch", file=sys.stderr, flush=True)
+        from block_sparse_long_04_amd.inputs import make_batch
+        del layer
+        res["varlen_batch"] = varlen_batch(cfg, _lib, make_batch, kept_pairs, torch, np)
     print(json.dumps(res), flush=True)
 
 
