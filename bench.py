@@ -233,6 +233,20 @@ def select_baselines(pf, _lib, torch, thr_ms, k, p, reps=5):
         ms = sorted(ts)[reps // 2]
         out[name] = {"param": param, "ms": round(ms, 4), "vs_threshold": round(ms / thr_ms, 2),
                      "kept_blocks": int(pf.ws.counts().sum().item())}
+    if pf.ws.nb <= 1024 and pf.prob.dtype != _lib.FP_F32:
+        # the query-probe reading of stage 1 (token-level max per key block)
+        pf.select_probe()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pf.select_probe()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[reps // 2]
+        out["probe_max"] = {"ms": round(ms, 4), "vs_threshold": round(ms / thr_ms, 2),
+                            "kept_blocks": int(pf.ws.counts().sum().item())}
     return out
 
 

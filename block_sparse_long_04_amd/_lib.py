@@ -23,7 +23,7 @@ FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP = 0, -1,
 FP_SELECT_TOPK, FP_SELECT_TOPP = 1, 2
 
 EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_sorted",
-            "fp_sparse_prefill", "fp_workspace_layout_varlen", "fp_block_pool_varlen",
+            "fp_block_select_probe", "fp_sparse_prefill", "fp_workspace_layout_varlen", "fp_block_pool_varlen",
             "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_strerror")
 
 
@@ -83,7 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, W = ctypes.POINTER(FpProblem), ctypes.POINTER(FpWsLayout)
     lib.fp_workspace_layout.argtypes = [P, W]
     lib.fp_workspace_layout.restype = ctypes.c_int
-    for name in ("fp_block_pool", "fp_block_select", "fp_sparse_prefill"):
+    for name in ("fp_block_pool", "fp_block_select", "fp_block_select_probe", "fp_sparse_prefill"):
         fn = getattr(lib, name)
         fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -137,6 +137,11 @@ def fp_block_select_sorted(prob: FpProblem, rule: int, param: float, ws_ptr: int
                            stream: int) -> None:
     _check(load_library().fp_block_select_sorted(ctypes.byref(prob), rule, param, ws_ptr, ws_bytes,
                                                  stream), "fp_block_select_sorted")
+
+
+def fp_block_select_probe(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_block_select_probe(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
+           "fp_block_select_probe")
 
 
 def fp_sparse_prefill(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
@@ -313,6 +318,11 @@ class Prefill:
         """Top-k (rule FP_SELECT_TOPK, param = k) or top-p (FP_SELECT_TOPP,
         param = p) selection into the same workspace sections as select()."""
         fp_block_select_sorted(self.prob, rule, param, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def select_probe(self):
+        """Query-probe selection (token-level max per key block) into the same
+        workspace sections as select()."""
+        fp_block_select_probe(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
 
     def attend(self):
         fp_sparse_prefill(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())

@@ -250,6 +250,23 @@ int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* wor
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 
+int fp_block_select_probe(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (p->dtype == FP_F32 || dm.d != 128 || dm.B != 128 || dm.nb > 1024) return FP_ERR_UNSUPPORTED;
+  if (dm.L == 0) return FP_OK;
+  if (!p->k || !aligned16(p->k)) return FP_ERR_INVALID;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const float lt = p->threshold == 0.f ? -INFINITY : (float)log((double)p->threshold);
+  const hipError_t e = fpk_launch_probe_select(*p, dm, at<float>(workspace, w.q_pool), eff_sm_scale(p), lt,
+                                               at<float>(workspace, w.row_max), at<int>(workspace, w.counts),
+                                               at<int>(workspace, w.indices), (hipStream_t)stream);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
   FpDims dm;
   int rc = check_problem(p, &dm);

@@ -65,6 +65,9 @@ hipError_t fpk_launch_select_sorted(const FpDims& dm, const float* q_pool, const
                                     float sm_scale, int rule, float param, float* row_max,
                                     int* counts, int* indices, hipStream_t st);
 
+hipError_t fpk_launch_probe_select(const fp_problem& p, const FpDims& dm, const float* q_pool, float sm_scale,
+                                   float ln_tau, float* row_max, int* counts, int* indices, hipStream_t st);
+
 hipError_t fpk_launch_vtrans(const fp_problem& p, const FpDims& dm, uint16_t* v_t, hipStream_t st);
 
 hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int* counts,

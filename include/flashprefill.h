@@ -140,6 +140,16 @@ typedef enum { FP_SELECT_TOPK = 1, FP_SELECT_TOPP = 2 } fp_select_rule;
 int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Query-probe reading of stage 1 (FlashPrefill skill page, "Core Concept":
+ * query probes, search cost O(L^2/B) against O((L/B)^2)): the pooled probe of
+ * query block i scored against every key token t of block j, reduced by the
+ * max, S'[h,i,j] = max_t (Qbar[h,i] . k[t]) * sm_scale, then the same
+ * threshold, diagonal and lists as fp_block_select.  Reads q_pool (from
+ * fp_block_pool) and k; writes row_max (of S'), counts and indices.  For bf16
+ * and e4m3 inputs with head_dim 128 and block_size 128, nb <= 1024
+ * (FP_ERR_UNSUPPORTED otherwise). */
+int fp_block_select_probe(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Step 5.  Reads q, k, v (or v_t, written by fp_block_pool), counts and
  * indices; writes out.  Must follow fp_block_pool on the same workspace. */
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);

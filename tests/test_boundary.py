@@ -246,3 +246,21 @@ def test_varlen_layout_and_host_validation():
     ve, _, _ = _varlen([0, 0])
     for fn in (fp.fp_block_pool_varlen, fp.fp_block_select_varlen, fp.fp_sparse_prefill_varlen):
         fn(prob(seq_len=0), ve, 0, 0, 0)
+
+
+def test_probe_selection_shapes_checked_before_launch():
+    fake = 1 << 20
+    for kw, code in ((dict(dtype=fp.FP_F32), fp.FP_ERR_UNSUPPORTED), (dict(head_dim=64), fp.FP_ERR_UNSUPPORTED),
+                     (dict(seq_len=1025 * 128), fp.FP_ERR_UNSUPPORTED)):
+        p = prob(**kw)
+        p.q, p.k, p.v, p.out = fake, fake, fake, fake
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fp.fp_block_select_probe(p, fake, 1 << 40, 0)
+        assert e.value.code == code, kw
+    p = prob()
+    lay = fp.fp_workspace_layout(p)
+    p.q, p.k, p.v, p.out = fake, fake, fake, fake
+    with pytest.raises(fp.FlashPrefillError) as e:
+        fp.fp_block_select_probe(p, fake, lay.total - 1, 0)
+    assert e.value.code == fp.FP_ERR_WORKSPACE
+    fp.fp_block_select_probe(prob(seq_len=0), 0, 0, 0)
