@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the batch (varlen, paged K/V) measurement of the default workload")
+    ap.add_argument("--select", choices=("threshold", "group"), default="threshold",
+                    help="selection of the timed step: each head's own threshold lists, or one "
+                         "union list per kv group (fp_block_select_group)")
+    ap.add_argument("--no-group", action="store_true",
+                    help="skip the group-shared selection measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -250,6 +255,37 @@ def select_baselines(pf, _lib, torch, thr_ms, k, p, reps=5):
     return out
 
 
+def group_select(pf, torch, kept_pairs, cfg, per_head, reps=5):
+    """Group-shared selection (fp_block_select_group: each head's own
+    threshold, then one union list per kv group) and the attention on its
+    lists, median of `reps` runs each, against the per-head figures of the
+    same run (per_head: stage_ms of the timed steps)."""
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[reps // 2]
+
+    sel_ms = timed(pf.select_group)
+    att_ms = timed(pf.attend)
+    counts = pf.ws.counts().cpu().numpy()
+    nb = cfg.num_blocks
+    flops = 4.0 * cfg.head_dim * kept_pairs(counts, cfg.seq_len, cfg.block_size)
+    layer_ms = per_head["pool"] + sel_ms + att_ms
+    return {"select_ms": round(sel_ms, 4), "attention_ms": round(att_ms, 4),
+            "ms_per_layer": round(layer_ms, 4),
+            "density": round(float(counts.sum()) / (cfg.num_q_heads * nb * (nb + 1) / 2), 5),
+            "kept_tflop": round(flops / 1e12, 4),
+            "attention_tflops": round(flops / (att_ms * 1e-3) / 1e12, 2),
+            "vs_per_head_ms_per_layer": round(layer_ms / sum(per_head.values()), 3)}
+
+
 # a serving-like mix of prompts: 4 of about 8K, 8 of 4K, 16 of 2K, 32 of 1K
 # tokens (ragged lengths), 128K tokens in all
 VARLEN_LENS = tuple([8192 - 37 * k for k in range(4)] + [4096 - 29 * k for k in range(8)] +
@@ -325,13 +361,15 @@ def main():
                       q_scale=layer.q_scale, k_scale=layer.k_scale, v_scale=layer.v_scale)
     layer.out = pf.out
 
+    select = pf.select_group if args.select == "group" else pf.select
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
         pf.pool()
         if ev is not None:
             ev[1].record()
-        pf.select()
+        select()
         if ev is not None:
             ev[2].record()
         pf.attend()
@@ -369,7 +407,7 @@ def main():
     sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2
     attn_tflops = flops / (stage_ms["attention"] * 1e-3) / 1e12
     peak = PEAK["fp8"] if cfg.dtype == "fp8" else PEAK["bf16"]
-    wl = cfg.name + f"_tau{tau:g}"
+    wl = cfg.name + f"_tau{tau:g}" + ("_group" if args.select == "group" else "")
     traffic = measured_traffic(wl)
     res = {
         "metric": METRIC,
@@ -404,7 +442,7 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.select == "threshold":  # its sample checks per-head lists
         print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
         idx = pf.ws.indices()
         tri = lambda h, i: h * (nb * (nb + 1) // 2) + i * (i + 1) // 2  # noqa: E731
@@ -420,7 +458,12 @@ def main():
         # mean kept count, top-p at 0.9)
         k_match = max(1, int(round(float(counts.mean()))))
         res["select_baselines"] = select_baselines(pf, _lib, torch, stage_ms["select"], k_match, 0.9)
-        pf.select()  # leave the threshold's lists in the workspace
+        select()  # leave the step's lists in the workspace
+    if not args.no_group and args.select == "threshold" and Hq > Hkv and tau > 0:
+        # one list per kv group (the union of its heads' selections)
+        print("[bench] group-shared selection", file=sys.stderr, flush=True)
+        res["group_select"] = group_select(pf, torch, kept_pairs, cfg, stage_ms)
+        pf.select()
     if not args.no_varlen and args.config == "c4":
         # a batch of sequences with K/V in pages, totalling about the same tokens
         print("[bench] varlen batch", file=sys.stderr, flush=True)

@@ -22,7 +22,8 @@ FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP = 0, -1,
 
 FP_SELECT_TOPK, FP_SELECT_TOPP = 1, 2
 
-EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_sorted",
+EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_group",
+            "fp_block_select_sorted",
             "fp_block_select_probe", "fp_sparse_prefill", "fp_workspace_layout_varlen", "fp_block_pool_varlen",
             "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_strerror")
 
@@ -83,7 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, W = ctypes.POINTER(FpProblem), ctypes.POINTER(FpWsLayout)
     lib.fp_workspace_layout.argtypes = [P, W]
     lib.fp_workspace_layout.restype = ctypes.c_int
-    for name in ("fp_block_pool", "fp_block_select", "fp_block_select_probe", "fp_sparse_prefill"):
+    for name in ("fp_block_pool", "fp_block_select", "fp_block_select_group", "fp_block_select_probe",
+                 "fp_sparse_prefill"):
         fn = getattr(lib, name)
         fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -131,6 +133,11 @@ def fp_block_pool(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> N
 def fp_block_select(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check(load_library().fp_block_select(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
            "fp_block_select")
+
+
+def fp_block_select_group(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_block_select_group(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
+           "fp_block_select_group")
 
 
 def fp_block_select_sorted(prob: FpProblem, rule: int, param: float, ws_ptr: int, ws_bytes: int,
@@ -313,6 +320,12 @@ class Prefill:
 
     def select(self):
         fp_block_select(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def select_group(self):
+        """Group-shared selection (each head's own threshold, then the union
+        over the heads of each kv group as every head's list) into the same
+        workspace sections as select()."""
+        fp_block_select_group(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
 
     def select_sorted(self, rule: int, param: float):
         """Top-k (rule FP_SELECT_TOPK, param = k) or top-p (FP_SELECT_TOPP,

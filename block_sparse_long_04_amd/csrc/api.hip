@@ -7,6 +7,10 @@
 #include "common.h"
 #include "varlen.h"
 
+// group.hip: union of the G heads' lists of each (kv group, query block),
+// written back as the list of every head of the group (in place).
+hipError_t fpk_launch_group_union(const FpDims& dm, int* counts, int* indices, hipStream_t st);
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -223,6 +227,26 @@ int fp_block_select(const fp_problem* p, void* workspace, size_t workspace_bytes
                         eff_sm_scale(p), lt, at<float>(workspace, w.row_max),
                         at<int>(workspace, w.counts), at<int>(workspace, w.indices),
                         (hipStream_t)stream);
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_block_select_group(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (dm.L == 0) return FP_OK;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const float lt = p->threshold == 0.f ? -INFINITY : (float)log((double)p->threshold);
+  hipError_t e =
+      fpk_launch_select(dm, at<float>(workspace, w.q_pool), at<float>(workspace, w.k_pool),
+                        eff_sm_scale(p), lt, at<float>(workspace, w.row_max),
+                        at<int>(workspace, w.counts), at<int>(workspace, w.indices),
+                        (hipStream_t)stream);
+  if (e == hipSuccess && dm.Hq > dm.Hkv)
+    e = fpk_launch_group_union(dm, at<int>(workspace, w.counts), at<int>(workspace, w.indices),
+                               (hipStream_t)stream);
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 

@@ -122,6 +122,20 @@ int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, 
  * block score matrix is never stored. */
 int fp_block_select(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Group-shared selection: one list per kv group, shared by its G = Hq/Hkv
+ * query heads (FlashPrefill V2 abstract: PackGQA, the heads of a group read
+ * the same K/V tiles; VSPrefill, Figure 3: heads of one kv group select
+ * closely similar blocks).  Each head first selects with its own threshold
+ * exactly as fp_block_select (row_max keeps each head's own maximum); then
+ * the union of the G heads' kept blocks of each (group, query block) is
+ * written as the list and count of every head of the group (ascending, ending
+ * with the diagonal).  Every head thus attends over a superset of its own
+ * selection, and the G workgroups of one (group, query block) walk identical
+ * lists, so each K/V tile they read is fetched once into L2 for all of them.
+ * fp_sparse_prefill runs on the result unchanged.  With G = 1 this is
+ * fp_block_select.  Same sections, arguments and errors as fp_block_select. */
+int fp_block_select_group(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Selection rules that sort the block scores or accumulate their mass: the
  * baselines the single-pass threshold avoids (FlashPrefill skill page, "Core
  * Concept"; FlashPrefill abstract).  Same sections as fp_block_select: reads

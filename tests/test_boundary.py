@@ -128,7 +128,7 @@ def test_entry_points_reject_before_launch():
         fp.fp_block_pool(p, fake, lay.total, 0)  # q/k are NULL
     assert e.value.code == fp.FP_ERR_INVALID
     p.q, p.k, p.v, p.out = fake, fake, fake, fake
-    for fn in (fp.fp_block_pool, fp.fp_block_select, fp.fp_sparse_prefill):
+    for fn in (fp.fp_block_pool, fp.fp_block_select, fp.fp_block_select_group, fp.fp_sparse_prefill):
         with pytest.raises(fp.FlashPrefillError) as e:
             fn(p, 0, lay.total, 0)
         assert e.value.code == fp.FP_ERR_WORKSPACE
@@ -147,9 +147,19 @@ def test_entry_points_reject_before_launch():
 def test_empty_problem_is_a_no_op():
     p = prob(seq_len=0)
     lay = fp.fp_workspace_layout(p)
-    for fn in (fp.fp_block_pool, fp.fp_block_select, fp.fp_sparse_prefill):
+    for fn in (fp.fp_block_pool, fp.fp_block_select, fp.fp_block_select_group, fp.fp_sparse_prefill):
         fn(p, 0, 0, 0)  # nothing launched, nothing read
     assert lay.total == 0
+
+
+def test_group_selection_validates_like_the_main_selection():
+    fake = 1 << 20
+    for field, value, code in (("threshold", 1.5, fp.FP_ERR_INVALID), ("num_kv_heads", 3, fp.FP_ERR_INVALID),
+                               ("causal", 0, fp.FP_ERR_UNSUPPORTED)):
+        p = prob(**{field: value})
+        with pytest.raises(fp.FlashPrefillError) as e:
+            fp.fp_block_select_group(p, fake, 1 << 40, 0)
+        assert e.value.code == code, field
 
 
 def test_strerror_texts():
