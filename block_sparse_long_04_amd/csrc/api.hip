@@ -70,13 +70,13 @@ int check_problem(const fp_problem* p, FpDims* dm) {
 }
 
 // The matrix-core attention serves bf16 and e4m3 inputs with d = B = 128.
-// It addresses one kv head of K through 32-bit buffer offsets, so every key
-// row of the padded sequence must start below 2^31 bytes from the head's
-// base; larger token strides go to the generic kernel.
+// It addresses K one key block at a time through 32-bit buffer offsets, so
+// the 128 rows of a block must span less than 2^31 bytes; token strides
+// beyond that (16 MiB per token) go to the generic kernel.
 bool use_mfma(const fp_problem* p, const FpDims& dm) {
   if (p->dtype == FP_F32 || dm.d != 128 || dm.B != 128) return false;
   const int64_t esz = p->dtype == FP_BF16 ? 2 : 1;
-  return (int64_t)dm.nb * dm.B * p->k_stride_tok * esz + dm.d * esz < (int64_t(1) << 31);
+  return (int64_t)dm.B * p->k_stride_tok * esz + dm.d * esz < (int64_t(1) << 31);
 }
 
 void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {

@@ -410,20 +410,22 @@ __device__ __forceinline__ void qk_unit(const uint4* sK, const QFrag<kFp8>& qf, 
 //   V^T: 128 rows (head dims) of 64 keys = 128 B (8 chunks of 8 keys);
 //      load e of wave w fills rows 32w + 8e + l/8, slot l%8 <- chunk
 //      (l%8) ^ swz8(row).
-// A buffer resource per kv head holds the base; the per-lane offsets are
-// fixed for the workgroup and a unit only moves the scalar offset, so a load
-// costs no vector address arithmetic.  (Buffer loads also keep LDS-read
-// waits exact: while a flat or global LDS load is in flight the compiler can
-// only wait for every LDS read, which would serialise the operand prefetch of
-// the matrix products.)  The host guarantees every offset of a kv head fits
-// in 31 bits.
+// The per-lane offsets are fixed for the workgroup and a unit only moves
+// scalar values, so a load costs no vector address arithmetic.  K is reached
+// through a buffer resource based at its key block (64-bit scalar address,
+// extent up to the block's last present row), so offsets stay below one
+// block's rows whatever the sequence length; V^T through one resource per kv
+// head (at most 2^21 keys of 128 dims: 512 MiB).  (Buffer loads also keep
+// LDS-read waits exact: while a flat or global LDS load is in flight the
+// compiler can only wait for every LDS read, which would serialise the
+// operand prefetch of the matrix products.)
 template <bool kFp8>
 struct TileLoader {
   static constexpr int kEsz = kFp8 ? 1 : 2;
   static constexpr int kKLoads = kFp8 ? 2 : 4;  // K loads per wave per unit
-  __amdgpu_buffer_rsrc_t krs;  // K of kv head g
+  const uint8_t* kg;           // K of kv head g
   __amdgpu_buffer_rsrc_t vrs;  // V^T rows of kv head g
-  int k_tile;                  // bytes between consecutive key blocks of K
+  int64_t k_tile;              // bytes between consecutive key blocks of K
   int k_row;                   // bytes between consecutive keys
   uint32_t koff[kKLoads], voff[4];
   int L;
@@ -438,11 +440,9 @@ struct TileLoader {
 
   __device__ __forceinline__ void init(const AttnArgs& a, int g, int w, int lane) {
     k_row = (int)(a.k_st * kEsz);
-    k_tile = 128 * k_row;
+    k_tile = 128 * (int64_t)k_row;
     L = a.L;
-    const int k_extent = (a.L - 1) * k_row + 128 * kEsz;
-    krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k + (int64_t)g * a.k_sh * kEsz), 0,
-                                            k_extent, 0x00020000);
+    kg = a.k + (int64_t)g * a.k_sh * kEsz;
     vrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.vt + (int64_t)g * 128 * a.Lpad), 0, 128 * a.Lpad * 2, 0x00020000);
 #pragma unroll
@@ -458,21 +458,23 @@ struct TileLoader {
   }
   // K half tile hf of key block j
   __device__ __forceinline__ void load_k(uint4* sK, int j, int hf, int w) const {
-    if (j * 128 + 64 * hf + 64 <= L) {
-      const int soff = j * k_tile + hf * 64 * k_row;
+    const int rows = min(128, L - j * 128);  // key rows present in block j
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kg + j * k_tile), 0, (rows - 1) * k_row + 128 * kEsz, 0x00020000);
+    if (64 * hf + 64 <= rows) {
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
-                                                 koff[e], soff, 0, 0);
+                                                 koff[e], hf * 64 * k_row, 0, 0);
     } else {  // ragged last block: rows past L repeat row L-1 (masked later)
       const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e) {
         const int row = krow_of(w, e, lane);
-        const int r = min(64 * hf + row, L - 1 - j * 128);
+        const int r = min(64 * hf + row, rows - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + (kKLoads * w + e) * 64), 16,
-                                                 (uint32_t)(r * k_row + kchunk_of(row, lane) * 16),
-                                                 j * k_tile, 0, 0);
+                                                 (uint32_t)(r * k_row + kchunk_of(row, lane) * 16), 0, 0,
+                                                 0);
       }
     }
   }

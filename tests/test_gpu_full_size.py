@@ -110,3 +110,73 @@ def test_full_size_sampled_parity(name, tau):
         f"{counts.sum() / (Hq * nb * (nb + 1) / 2):.4f}")
     assert sel_bad == 0
     assert worst <= tmax and sum_abs / n_abs <= tmean
+
+
+def test_maximum_block_count_2m_tokens():
+    """The largest layer the library takes: 16384 blocks of 128 tokens (2M
+    tokens), 32 q / 8 kv heads, bf16.  One kv head of K then spans 4 GiB of
+    token-major memory, so the attention must address K per key block.
+    Whole-layer list shape everywhere; sampled rows of two kv groups against
+    the oracle (selection and attention)."""
+    dev = require_gpu()
+    nbmax = 16384
+    cfg = CONFIGS["c4"].with_(seq_len=nbmax * 128)
+    tau = 0.1
+    L, B, Hq, Hkv, d = cfg.seq_len, cfg.block_size, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    G, nb = Hq // Hkv, cfg.num_blocks
+    assert nb == nbmax
+    say(f"[max size] L={L} nb={nb} {cfg.dtype}; K spans {L * Hkv * d * 2 / 2**30:.0f} GiB")
+    lay = make_layer(cfg, device=dev, keep_fp32=False)
+    pf = _lib.Prefill(lay.q, lay.k, lay.v, block_size=B, threshold=tau)
+    pf.run()
+    torch.cuda.synchronize()
+    say("    layer done")
+    counts = pf.ws.counts()
+    idx = pf.ws.indices()
+    ii = torch.arange(nb, device=dev, dtype=torch.int64)
+    assert bool(((counts >= 1) & (counts <= ii[None, :] + 1)).all())
+    # every list ends with its diagonal block
+    hh = torch.arange(Hq, device=dev, dtype=torch.int64)[:, None]
+    last = hh * (nb * (nb + 1) // 2) + ii * (ii + 1) // 2 + counts.long() - 1
+    assert bool((idx[last] == ii[None, :].int()).all())
+    density = float(counts.sum()) / (Hq * nb * (nb + 1) / 2)
+    cnt = counts.cpu().numpy()
+    row_max = pf.ws.row_max().cpu().numpy()
+    sc = 1.0 / math.sqrt(d)
+    worst = sum_abs = 0.0
+    n_abs = sel_bad = 0
+    rng = np.random.default_rng(7)
+    qfull = np.zeros((L, 1, d), np.float32)
+    for g in (0, Hkv - 1):
+        kh = lay.k[:, g:g + 1].float().cpu().numpy()
+        vh = lay.v[:, g:g + 1].float().cpu().numpy()
+        kbar = O.pool(kh, B)  # [1, nb, d]
+        rows = [(g * G, nb - 1), (g * G + G - 1, 0), (g * G + 1, nb // 2)]
+        rows += [(g * G + int(u), int(i)) for u, i in zip(rng.integers(0, G, 3), rng.integers(0, nb, 3))]
+        for (h, i) in rows:
+            s0, s1 = i * B, (i + 1) * B
+            qrows = lay.q[s0:s1, h:h + 1].float().cpu().numpy()
+            qbar = O.pool(qrows, B)[0, 0]
+            kept, m, srow, amb = O.select_rows(qbar[None], kbar, [(0, i)], tau, sc, 1)[0]
+            assert abs(row_max[h, i] - m) <= 1e-5 * max(1.0, abs(float(m)))
+            off = h * (nb * (nb + 1) // 2) + i * (i + 1) // 2
+            gl = idx[off: off + int(cnt[h, i])].cpu().numpy()
+            got = np.zeros(i + 1, bool)
+            got[gl] = True
+            want = np.zeros(i + 1, bool)
+            want[kept] = True
+            sel_bad += int(((got != want) & ~amb).sum())
+            qfull[s0:s1] = qrows
+            ref = O.attend_row_block(qfull, kh, vh, 0, i, gl, B, sc, 1)
+            qfull[s0:s1] = 0.0
+            out = pf.out[s0:s1, h, :].float().cpu().numpy()
+            dd = np.abs(out - ref)
+            worst = max(worst, float(dd.max()))
+            sum_abs += float(dd.sum())
+            n_abs += dd.size
+        del kh, vh
+    say(f"    density {density:.4f}; sampled rows: selection mismatches {sel_bad}; "
+        f"out max-abs {worst:.3e} mean-abs {sum_abs / n_abs:.3e}")
+    assert sel_bad == 0
+    tmax, tmean = TOL["bf16"]
+    assert worst <= tmax and sum_abs / n_abs <= tmean
