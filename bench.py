@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--config", default="c4",
                     help="workload key: c1 c2 c3 c4 c4_fp8 c4_dense c5")
     ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--evict-mib", type=int, default=512,
+                    help="before each timed step, outside its events, write a buffer of this many "
+                         "MiB so the Infinity Cache (256 MiB) holds none of the previous step's data "
+                         "(0: off)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -381,9 +385,12 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evict = torch.empty(args.evict_mib << 20, dtype=torch.uint8, device=dev) if args.evict_mib > 0 else None
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for k in range(args.steps):
+        if evict is not None:
+            evict.fill_(k & 0xFF)  # same stream, before the step's first event
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -393,7 +400,8 @@ def main():
         st["select"].append(ev[1].elapsed_time(ev[2]))
         st["attention"].append(ev[2].elapsed_time(ev[3]))
     stage_ms = {k: float(np.mean(v)) for k, v in st.items()}
-    ms_step = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    per_step = [ev[0].elapsed_time(ev[3]) for ev in evs]
+    ms_step = float(np.mean(per_step))
     counts = pf.ws.counts().cpu().numpy()
     L, B, d, Hq, Hkv = cfg.seq_len, cfg.block_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
     nb = cfg.num_blocks
@@ -418,7 +426,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_layer": round(ms_step, 4),
+        "ms_per_step_median": round(float(np.median(per_step)), 4),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "infinity_cache_evicted_mib": args.evict_mib,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
