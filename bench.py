@@ -44,7 +44,7 @@ def parse():
                     help="workload key: c1 c2 c3 c4 c4_fp8 c4_dense c5")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--evict-mib", type=int, default=512,
-                    help="before each timed step, outside its events, write a buffer of this many "
+                    help="before each timed step, outside its events, read a buffer of this many "
                          "MiB so the Infinity Cache (256 MiB) holds none of the previous step's data "
                          "(0: off)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -385,12 +385,16 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    evict = torch.empty(args.evict_mib << 20, dtype=torch.uint8, device=dev) if args.evict_mib > 0 else None
+    # Eviction reads a buffer: written lines would leave dirty data in the
+    # cache whose write-back then competes with the step's first reads.
+    evict = torch.ones(args.evict_mib << 20, dtype=torch.uint8, device=dev) if args.evict_mib > 0 else None
+    if evict is not None:
+        evict.max()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for k in range(args.steps):
         if evict is not None:
-            evict.fill_(k & 0xFF)  # same stream, before the step's first event
+            evict.max()  # same stream, before the step's first event
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
