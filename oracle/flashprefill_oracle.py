@@ -224,7 +224,7 @@ def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale
 
 
 # ---------------------------------------------------------------------------
-# Whole-layer driver.
+# Whole-layer pipeline.
 # ---------------------------------------------------------------------------
 
 def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_size: int, tau: float,
