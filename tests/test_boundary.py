@@ -274,3 +274,24 @@ def test_probe_selection_shapes_checked_before_launch():
         fp.fp_block_select_probe(p, fake, lay.total - 1, 0)
     assert e.value.code == fp.FP_ERR_WORKSPACE
     fp.fp_block_select_probe(prob(seq_len=0), 0, 0, 0)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    # a fresh interpreter pointed at a missing library: loading raises, and
+    # there is no fallback path that would compute anything on the host
+    code = (
+        "import sys\n"
+        "from block_sparse_long_04_amd import _lib\n"
+        "try:\n"
+        f"    _lib.load_library({str(tmp_path / 'absent.so')!r})\n"
+        "except FileNotFoundError as e:\n"
+        "    print('raised', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(1)\n"
+    )
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "raised" in r.stdout
