@@ -418,7 +418,10 @@ def main():
                   + ((L * Hkv * d * esz + Hkv * d * nb * B * 2) if mfma_path else 0))
     sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2
     attn_tflops = flops / (stage_ms["attention"] * 1e-3) / 1e12
-    peak = PEAK["fp8"] if cfg.dtype == "fp8" else PEAK["bf16"]
+    # matrix-core attention for bf16 / e4m3 with d = B = 128; otherwise the
+    # generic kernel, fp32 vector ALUs
+    bound = "mfma" if mfma_path else "alu"
+    peak = PEAK["fp8"] if cfg.dtype == "fp8" else (PEAK["bf16"] if mfma_path else PEAK["fp32"])
     wl = cfg.name + f"_tau{tau:g}" + ("_group" if args.select == "group" else "")
     traffic = measured_traffic(wl)
     res = {
@@ -451,7 +454,7 @@ def main():
         "pool_gbs": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
         "pool_hbm_frac": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK["hbm_gbs"], 4),
         "select_tflops_fp32": round(sel_flops / (stage_ms["select"] * 1e-3) / 1e12, 2),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+        "roofline": {"bound": bound, "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": traffic},
         "cpu_baseline": None,

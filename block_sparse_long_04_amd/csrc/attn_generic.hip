@@ -1,12 +1,14 @@
 // Step 5 on the vector ALUs: block-sparse causal attention for the shapes
 // the matrix-core kernel does not take (fp32 inputs, head_dim 64, block 64,
-// and e4m3fn inputs until their matrix-core kernel lands).
+// token strides too large for its 32-bit tile offsets).
 //
 // FlashPrefill skill page, "Architecture Overview" (physical index jumping
-// over the kept block indices).  One workgroup = one (q head, query block),
-// one thread per query row.  For each listed key block the K and V tiles are
-// widened to fp32 in LDS; every thread runs an exact per-key online softmax
-// (running max, rescaled sum and accumulator) in fp32 with expf.
+// over the kept block indices).  One workgroup = one (q head, query block):
+// KS threads per query row, each taking every KS-th key of the listed blocks.
+// For each listed key block the K and V tiles are widened to fp32 in LDS;
+// every thread runs an exact per-key online softmax (running max, rescaled
+// sum and accumulator) in fp32 with expf over its keys, and at the end the
+// KS partial states of a row are merged (max, rescale, sum).
 #include "common.h"
 
 namespace {
@@ -33,13 +35,16 @@ __device__ __forceinline__ float load_elem(const uint8_t* p, int64_t idx) {
 }
 
 template <int D, int BS, int ESZ>
-__global__ __launch_bounds__(BS) void attn_generic_kernel(GenArgs a) {
+__global__ __launch_bounds__(256) void attn_generic_kernel(GenArgs a) {
+  constexpr int KS = 256 / BS;  // threads per query row: 4 for B = 64, 2 for B = 128
   __shared__ float sK[BS][D];
   __shared__ float sV[BS][D];
+  __shared__ float sML[BS][2];
   const int h = blockIdx.x % a.Hq;
   const int i = a.nb - 1 - (int)(blockIdx.x / a.Hq);
   const int g = h / (a.Hq / a.Hkv);
-  const int t = threadIdx.x;
+  const int t = threadIdx.x % BS;   // query row of the block
+  const int part = threadIdx.x / BS;  // this thread takes keys s with s % KS == part
   const int tq = i * BS + t;
   const bool valid = tq < a.L;
 
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(BS) void attn_generic_kernel(GenArgs a) {
   for (int n = 0; n < cnt; ++n) {
     const int j = lst[n];
     __syncthreads();
-    for (int e = t; e < BS * D; e += BS) {
+    for (int e = threadIdx.x; e < BS * D; e += BS * KS) {
       const int r = e / D;
       const int c = e - r * D;
       const int key = j * BS + r;
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(BS) void attn_generic_kernel(GenArgs a) {
     int kend = (j == i) ? t : BS - 1;       // causal inside the diagonal block
     kend = min(kend, a.L - 1 - j * BS);     // keys past L do not exist
     if (!valid) kend = -1;
-    for (int s = 0; s <= kend; ++s) {
+    for (int s = part; s <= kend; s += KS) {
       float x = 0.f;
 #pragma unroll
       for (int c = 0; c < D; ++c) x = fmaf(qv[c], sK[s][c], x);
@@ -91,7 +96,29 @@ __global__ __launch_bounds__(BS) void attn_generic_kernel(GenArgs a) {
       for (int c = 0; c < D; ++c) o[c] = fmaf(p, sV[s][c], o[c]);
     }
   }
-  if (!valid) return;
+  // merge the KS partial states of each row into part 0, one part at a
+  // time through sK (a part with no keys has m = -inf and l = 0)
+  for (int p = 1; p < KS; ++p) {
+    __syncthreads();
+    if (part == p) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) sK[t][c] = o[c];
+      sML[t][0] = m;
+      sML[t][1] = l;
+    }
+    __syncthreads();
+    if (part == 0) {
+      const float m2 = sML[t][0], l2 = sML[t][1];
+      const float mn = fmaxf(m, m2);
+      const float a1 = mn == -INFINITY ? 0.f : expf(m - mn);
+      const float a2 = mn == -INFINITY ? 0.f : expf(m2 - mn);
+      l = l * a1 + l2 * a2;
+#pragma unroll
+      for (int c = 0; c < D; ++c) o[c] = o[c] * a1 + sK[t][c] * a2;
+      m = mn;
+    }
+  }
+  if (!valid || part != 0) return;
   const float inv = a.out_scale / l;
   if (a.out_f32) {
     float* op = static_cast<float*>(a.out) + (int64_t)tq * a.o_st + h * a.o_sh;
@@ -106,9 +133,10 @@ __global__ __launch_bounds__(BS) void attn_generic_kernel(GenArgs a) {
 
 template <int D, int BS>
 hipError_t launch_db(const GenArgs& a, int esz, unsigned grid, hipStream_t st) {
-  if (esz == 4) hipLaunchKernelGGL((attn_generic_kernel<D, BS, 4>), dim3(grid), dim3(BS), 0, st, a);
-  else if (esz == 2) hipLaunchKernelGGL((attn_generic_kernel<D, BS, 2>), dim3(grid), dim3(BS), 0, st, a);
-  else hipLaunchKernelGGL((attn_generic_kernel<D, BS, 1>), dim3(grid), dim3(BS), 0, st, a);
+  static_assert(256 % BS == 0, "block size divides the workgroup");
+  if (esz == 4) hipLaunchKernelGGL((attn_generic_kernel<D, BS, 4>), dim3(grid), dim3(256), 0, st, a);
+  else if (esz == 2) hipLaunchKernelGGL((attn_generic_kernel<D, BS, 2>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_generic_kernel<D, BS, 1>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
