@@ -454,6 +454,7 @@ def main():
         "pool_gbs": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
         "pool_hbm_frac": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK["hbm_gbs"], 4),
         "select_tflops_fp32": round(sel_flops / (stage_ms["select"] * 1e-3) / 1e12, 2),
+        "select_fp32_frac": round(sel_flops / (stage_ms["select"] * 1e-3) / 1e12 / PEAK["fp32"], 4),
         "roofline": {"bound": bound, "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": traffic},
