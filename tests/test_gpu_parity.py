@@ -16,7 +16,7 @@ import oracle.flashprefill_oracle as O
 from block_sparse_long_04_amd import _lib
 from block_sparse_long_04_amd.inputs import CONFIGS, make_layer
 from tests.parity_util import (check_lists_wellformed, check_out, check_pool, gpu_lists, oracle_full,
-                               require_gpu, run_gpu, say, selection_mismatch, sm_scale)
+                               require_gpu, run_gpu, say, selection_mismatch, sm_scale, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -229,3 +229,54 @@ def test_selection_work_splits(name):
         for row in lists:
             for i, lst in enumerate(row):
                 assert len(lst) == i + 1
+
+
+def test_tau_one_keeps_the_row_argmax_and_the_diagonal():
+    # ln(1) = 0: a block survives only at the row maximum (ties included)
+    # or on the diagonal.  Structured layer, plus a layer whose keys repeat
+    # one block's content so that several blocks tie exactly at the maximum.
+    dev = require_gpu()
+    cfg = CONFIGS["c2"].with_(seq_len=1500, num_q_heads=4, num_kv_heads=2)
+    say("[tau=1] L=1500")
+    layer = make_layer(cfg)
+    ref = oracle_full(layer, 1.0)
+    _, res = run_gpu(layer, 1.0, dev)
+    bad, _ = selection_mismatch(res["lists"], ref["keep"], ref["amb"])
+    assert bad == 0
+    nb = cfg.num_blocks
+    for h in range(4):
+        for i in range(nb):
+            assert 1 <= len(res["lists"][h][i]) <= 2 or ref["amb"][h, i].any()
+    want = O.sparse_attention(ref["q"], ref["k"], ref["v"], res["lists"], 128, sm_scale(layer))
+    check_out(res["out"], want, "bf16")
+
+    # exact ties: every key block holds the same 128 rows, so every full
+    # causal block of a row has the same proxy score.  The matrix cores do not
+    # return bit-identical fp32 results for identical inputs in different
+    # output columns, so which tied blocks reach the maximum is decided by
+    # rounding: every tied block lies in the tie zone, and the lists must
+    # still agree with the oracle outside it and end with the diagonal.
+    k32 = layer.k32.clone()
+    for j in range(1, nb):
+        n = min(128, 1500 - j * 128)
+        k32[j * 128: j * 128 + n] = layer.k32[:n]
+    q32, v32 = layer.q32.numpy(), layer.v32.numpy()
+    r = O.prefill(q32, k32.numpy(), v32, 128, 1.0, sm_scale(layer), attention=False)
+    amb = O.ambiguous(r["S"], r["row_max"], 1.0)
+    full = [j for j in range(nb) if (j + 1) * 128 <= 1500]
+    for h in range(4):
+        for i in full:
+            assert amb[h, i, :i].all(), (h, i)  # the construction really ties
+    q, _, v = to_dev(layer, dev)
+    pf = _lib.Prefill(q, k32.to(torch.bfloat16).to(dev), v, block_size=128, threshold=1.0)
+    pf.pool()
+    pf.select()
+    pf.attend()
+    torch.cuda.synchronize()
+    lists = gpu_lists(pf.ws.counts().cpu().numpy(), pf.ws.indices().cpu().numpy(), nb)
+    check_lists_wellformed(lists, nb)
+    bad, amb_diff = selection_mismatch(lists, r["keep"], amb)
+    say(f"    tie layer: {amb_diff} tied blocks decided differently from the oracle (allowed)")
+    assert bad == 0
+    want = O.sparse_attention(q32, k32.numpy(), v32, lists, 128, sm_scale(layer))
+    check_out(pf.out.float().cpu().numpy(), want, "bf16")
