@@ -33,6 +33,7 @@ CASES = {
     "fp8_ragged_8x2": ("c4_fp8", {"seq_len": 1500, "num_q_heads": 8, "num_kv_heads": 2}, 0.1),
     "f32_d64_b64_4x1": ("c1", {"recipe": "structured", "n_vertical": 4, "num_q_heads": 4}, 0.1),
     "bf16_mha": ("c2", {"seq_len": 777, "num_q_heads": 4, "num_kv_heads": 4}, 0.1),
+    "bf16_gqa3": ("c2", {"seq_len": 2000, "num_q_heads": 12, "num_kv_heads": 4}, 0.1),
 }
 
 

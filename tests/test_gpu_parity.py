@@ -33,6 +33,8 @@ CASES = {
     "fp8_ragged": ("c4_fp8", {"seq_len": 1000, "num_q_heads": 8, "num_kv_heads": 2}, 0.1),
     "f32_d128_b128": ("c2", {"seq_len": 700, "num_q_heads": 2, "num_kv_heads": 1,
                              "dtype": "f32"}, 0.1),
+    # three q heads per kv head and 4 kv heads: the attention's plain work order
+    "bf16_gqa3": ("c2", {"seq_len": 2000, "num_q_heads": 12, "num_kv_heads": 4}, 0.1),
 }
 
 
