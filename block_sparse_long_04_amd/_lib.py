@@ -277,6 +277,53 @@ class Workspace:
         import torch
         return self._view(self.layout.indices, self.Hq * self.nb * (self.nb + 1) // 2, torch.int32)
 
+    def set_lists(self, counts, indices) -> None:
+        """Write caller-made lists (host arrays: counts [Hq, nb], flat
+        triangular indices) into the workspace, after validate_lists."""
+        import numpy as np
+        import torch
+        validate_lists(counts, indices, self.nb)
+        tri = self.Hq * self.nb * (self.nb + 1) // 2
+        self.counts().copy_(torch.from_numpy(np.ascontiguousarray(counts, dtype=np.int32)))
+        self.indices().copy_(torch.from_numpy(np.ascontiguousarray(np.asarray(indices).reshape(-1)[:tri],
+                                                                   dtype=np.int32)))
+
+
+def validate_lists(counts, indices, nb: int) -> None:
+    """Host-side check of caller-written block lists before they go into a
+    workspace: for every (h, i), 1 <= counts[h, i] <= i + 1 and the entries
+    at indices[h*nb(nb+1)/2 + i(i+1)/2 ...] are strictly ascending, inside
+    [0, i] and end with i (the diagonal).  The attention kernels trust the
+    lists they are given, so a list that breaks these rules must never reach
+    them.  counts: [Hq, nb] int array; indices: the flat triangular array (or
+    at least its used entries).  Raises FlashPrefillError(FP_ERR_INVALID)."""
+    import numpy as np
+    counts = np.asarray(counts)
+    indices = np.asarray(indices).reshape(-1)
+    if counts.ndim != 2 or counts.shape[1] != nb:
+        raise FlashPrefillError(FP_ERR_INVALID, "validate_lists: counts shape")
+    Hq = counts.shape[0]
+    tri = nb * (nb + 1) // 2
+    if indices.size < Hq * tri:
+        raise FlashPrefillError(FP_ERR_INVALID, "validate_lists: indices too short")
+    i = np.arange(nb)
+    if (counts < 1).any() or (counts > i[None, :] + 1).any():
+        raise FlashPrefillError(FP_ERR_INVALID, "validate_lists: count outside [1, i + 1]")
+    row = np.repeat(i, i + 1)                        # row of every triangular slot
+    off = np.arange(tri) - (i * (i + 1) // 2)[row]   # slot within its row
+    for h in range(Hq):
+        sec = indices[h * tri:(h + 1) * tri].astype(np.int64)
+        used = off < counts[h][row]
+        e, r, o = sec[used], row[used], off[used]
+        if (e < 0).any() or (e > r).any():
+            raise FlashPrefillError(FP_ERR_INVALID, f"validate_lists: entry outside [0, i] (head {h})")
+        last = o == counts[h][r] - 1
+        if (e[last] != r[last]).any():
+            raise FlashPrefillError(FP_ERR_INVALID, f"validate_lists: list does not end with i (head {h})")
+        nxt = ~last
+        if (e[nxt] >= e[np.flatnonzero(nxt) + 1]).any():
+            raise FlashPrefillError(FP_ERR_INVALID, f"validate_lists: entries not ascending (head {h})")
+
 
 def alloc_workspace(prob: FpProblem, device) -> Workspace:
     import torch

@@ -1,8 +1,8 @@
 """Build the HIP library libflashprefill.so in-tree for gfx950.
 
 Usage: python -m block_sparse_long_04_amd.build  (or build_library() from Python).
-One hipcc invocation compiles every csrc/*.hip file (the kernels and the C
-ABI) into one shared library next to this file.
+hipcc compiles every csrc/*.hip file (the kernels and the C ABI), one
+process per file, and links them into one shared library next to this file.
 """
 from __future__ import annotations
 
@@ -41,10 +41,7 @@ def compile_flags() -> list:
     ]
 
 
-def build_library(verbose: bool = True, extra: list = None) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + compile_flags() + (extra or []) + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,7 +53,25 @@ def build_library(verbose: bool = True, extra: list = None) -> str:
         lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB_PATH)
+
+
+def build_library(verbose: bool = True, extra: list = None) -> str:
+    """Compile every csrc/*.hip to an object in parallel, then link them into
+    the shared library (each object carries its own gfx950 code object)."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    flags = [f for f in compile_flags() if f != "-shared"] + (extra or [])
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with tempfile.TemporaryDirectory(prefix="fpbuild_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda so: _run([hipcc()] + flags + ["-c", so[0], "-o", so[1]], verbose),
+                        zip(srcs, objs)))
+        tmp = LIB_PATH + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
 

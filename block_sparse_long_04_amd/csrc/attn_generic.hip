@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(GenArgs a) {
       const int c = e - r * D;
       const int key = j * BS + r;
       float kx = 0.f, vx = 0.f;
-      if (key < a.L) {
+      if (key >= 0 && key < a.L) {  // (j outside the sequence: zeros, never a stray read)
         kx = load_elem<ESZ>(a.k, (int64_t)key * a.k_st + g * a.k_sh + c);
         vx = load_elem<ESZ>(a.v, (int64_t)key * a.v_st + g * a.v_sh + c);
       }

@@ -459,8 +459,12 @@ struct TileLoader {
   // K half tile hf of key block j
   __device__ __forceinline__ void load_k(uint4* sK, int j, int hf, int w) const {
     const int rows = min(128, L - j * 128);  // key rows present in block j
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(kg + j * k_tile), 0, (rows - 1) * k_row + 128 * kEsz, 0x00020000);
+    // A list entry outside [0, nb) (a caller-written list that breaks the
+    // documented rules) gets an empty resource: its reads return zeros
+    // instead of leaving the tensor.
+    const int ext = (j >= 0 && rows > 0) ? (rows - 1) * k_row + 128 * kEsz : 0;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kg + j * k_tile), 0, ext, 0x00020000);
     if (64 * hf + 64 <= rows) {
 #pragma unroll
       for (int e = 0; e < kKLoads; ++e)

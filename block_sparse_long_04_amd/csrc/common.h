@@ -40,6 +40,17 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return __builtin_amdgcn_cvt_f32_fp8((int)(c & 0xffu), 0);
 }
 
+// S - m of the threshold rule with the score S = acc * scale rounded to fp32
+// first.  Contracting the two into one fused multiply-add would compare the
+// exact product against a row max taken from rounded products, so a block
+// whose score equals the row max could fall below it (FlashPrefill skill
+// page, "Core Concept" item 3: exp(S - m) >= tau with m the largest S).
+__device__ __forceinline__ float score_minus_max(float acc, float scale, float m) {
+#pragma clang fp contract(off)
+  const float s = acc * scale;
+  return s - m;
+}
+
 __host__ __device__ __forceinline__ int64_t tri_offset(int64_t h, int64_t i, int64_t nb) {
   return h * (nb * (nb + 1) / 2) + i * (i + 1) / 2;
 }

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool keep = (dl - r <= lim && 4 * grp + r < rows_left) &&
-                          ((acc[u][r] * scale - mu[r] >= ln_tau) || dl - r == lim);
+                          ((fpk::score_minus_max(acc[u][r], scale, mu[r]) >= ln_tau) || dl - r == lim);
         bits[r] = __ballot(keep);
       }
       if (jt <= rt_hi) put_masks(jt, u, bits);

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void select_varlen_kernel(const float* __restr
       const int row = 4 * grp + r;
       const int i = i0 + row;
       const bool keep = (j >= first_of[row] && j <= i && i < NB) &&
-                        ((acc[r] * scale - mrow[row] >= ln_tau) || j == i);
+                        ((fpk::score_minus_max(acc[r], scale, mrow[row]) >= ln_tau) || j == i);
       bits[r] = __ballot(keep);
     }
     if (lane < 16) {

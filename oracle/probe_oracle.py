@@ -62,3 +62,29 @@ def select_probe(q: np.ndarray, k: np.ndarray, block_size: int, tau: float, sm_s
     keep, m = O.select(S, tau)
     return dict(qbar=qbar, S=S, keep=keep, row_max=m, lists=O.block_lists(keep),
                 amb=O.ambiguous(S, m, tau))
+
+
+def probe_select_rows(qbar_rows: np.ndarray, k: np.ndarray, rows, block_size: int, tau: float,
+                      sm_scale: float, group: int):
+    """The probe selection of sampled (h, i) rows only (layers too large to
+    score whole).  qbar_rows[n] is Qbar[h_n, i_n, :]; k the [L, Hkv, d] key
+    tokens.  Each row's scores S'[h, i, :i+1] are taken as in probe_scores;
+    the row is then placed as the last row of an otherwise empty causal
+    triangle, so the main method's own select and ambiguous decide it.
+    Returns (kept ascending int32, row_max fp32, S' row fp32, ambiguous row)
+    in the order of ``rows``."""
+    L = k.shape[0]
+    scale = np.float32(sm_scale)
+    res = []
+    for n, (h, i) in enumerate(rows):
+        end = min((i + 1) * block_size, L)
+        tok = (k[:end, h // group].astype(np.float32) @ qbar_rows[n].astype(np.float32)) * scale
+        tok = tok.astype(np.float32)
+        srow = np.array([tok[j * block_size: min((j + 1) * block_size, end)].max() for j in range(i + 1)],
+                        dtype=np.float32)
+        S = np.full((1, i + 1, i + 1), -np.inf, dtype=np.float32)
+        S[0, i] = srow
+        keep, m = O.select(S, tau)
+        amb = O.ambiguous(S, m, tau)
+        res.append((np.flatnonzero(keep[0, i]).astype(np.int32), m[0, i], srow, amb[0, i]))
+    return res

@@ -59,8 +59,7 @@ def inject_lists(pf: _lib.Prefill, lists) -> None:
             counts[h, i] = len(lst)
             off = h * (nb * (nb + 1) // 2) + i * (i + 1) // 2
             idx[off: off + len(lst)] = lst
-    pf.ws.counts().copy_(torch.from_numpy(counts))
-    pf.ws.indices().copy_(torch.from_numpy(idx))
+    pf.ws.set_lists(counts, idx)
 
 
 def run_gpu(layer: Layer, tau: float, dev, lists=None, q=None, k=None, v=None, out=None):

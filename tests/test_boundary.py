@@ -295,3 +295,59 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stdout + r.stderr
     assert "raised" in r.stdout
+
+
+def _valid_lists(Hq, nb, seed=0):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    tri = nb * (nb + 1) // 2
+    counts = np.zeros((Hq, nb), np.int32)
+    idx = np.full(Hq * tri, -7, np.int32)  # unused slots hold garbage on purpose
+    for h in range(Hq):
+        for i in range(nb):
+            lst = sorted(set(rng.choice(i + 1, size=rng.integers(0, i + 1), replace=False).tolist()) | {i})
+            counts[h, i] = len(lst)
+            off = h * tri + i * (i + 1) // 2
+            idx[off: off + len(lst)] = lst
+    return counts, idx
+
+
+def test_list_validation_rejects_bad_lists_before_any_write():
+    """Caller-made lists are checked on the host (count in [1, i+1],
+    ascending, inside [0, i], ending with i) before they reach the
+    workspace; a bad list leaves the workspace untouched.  The workspace here
+    is host memory: no GPU is involved."""
+    import numpy as np
+    import torch
+    Hq, nb = 3, 9
+    p = prob(seq_len=nb * 128 - 50, num_q_heads=Hq, num_kv_heads=1)
+    ws = _lib.alloc_workspace(p, "cpu")
+    ws.buf.fill_(0)
+    counts, idx = _valid_lists(Hq, nb)
+    _lib.validate_lists(counts, idx, nb)
+    tri = nb * (nb + 1) // 2
+
+    def row_off(h, i):
+        return h * tri + i * (i + 1) // 2
+
+    bad = []
+    c = counts.copy(); c[1, 4] = 0; bad.append((c, idx))                       # empty list
+    c = counts.copy(); c[2, 3] = 5; bad.append((c, idx))                       # count > i + 1
+    x = idx.copy(); x[row_off(0, 6) + counts[0, 6] - 1] = 7; bad.append((counts, x))  # past i
+    x = idx.copy(); x[row_off(1, 8)] = -1; bad.append((counts, x))            # negative
+    h, i = 2, 8
+    c = counts.copy(); x = idx.copy()
+    lst = list(range(0, i + 1))
+    c[h, i] = len(lst); x[row_off(h, i): row_off(h, i) + len(lst)] = lst
+    _lib.validate_lists(c, x, nb)                                              # dense row is fine
+    y = x.copy(); y[row_off(h, i) + 3] = y[row_off(h, i) + 2]; bad.append((c, y))  # repeated entry
+    y = x.copy(); y[row_off(h, i) + 3], y[row_off(h, i) + 4] = 4, 3; bad.append((c, y))  # not ascending
+    c2 = c.copy(); c2[h, i] = i; bad.append((c2, x))                           # does not end with i
+    for cb, xb in bad:
+        with pytest.raises(_lib.FlashPrefillError) as e:
+            ws.set_lists(cb, xb)
+        assert e.value.code == _lib.FP_ERR_INVALID
+        assert int(ws.buf.sum()) == 0
+    ws.set_lists(counts, idx)
+    assert np.array_equal(ws.counts().numpy(), counts)
+    assert np.array_equal(ws.indices().numpy(), idx)

@@ -249,6 +249,22 @@ def test_tau_one_keeps_the_row_argmax_and_the_diagonal():
     for h in range(4):
         for i in range(nb):
             assert 1 <= len(res["lists"][h][i]) <= 2 or ref["amb"][h, i].any()
+    # The row's own maximum has S - m = 0 >= ln 1, so it is kept.  The
+    # argmax itself lies in the tie zone (|S - T| = 0), so the comparison
+    # above cannot see a dropped one; where the maximum lies clearly off the
+    # diagonal (by far more than the rounding of the scores), a list holding
+    # only the diagonal means the maximum was dropped.
+    S = ref["S"].astype(np.float64)
+    m = ref["row_max"].astype(np.float64)
+    clear = 0
+    for h in range(4):
+        for i in range(1, nb):
+            margin = 1e-3 * max(1.0, abs(m[h, i]))
+            if S[h, i, :i].max() >= S[h, i, i] + margin:
+                clear += 1
+                assert len(res["lists"][h][i]) >= 2, (h, i)
+    say(f"    {clear} rows with the maximum clearly off the diagonal keep it")
+    assert clear > 0
     want = O.sparse_attention(ref["q"], ref["k"], ref["v"], res["lists"], 128, sm_scale(layer))
     check_out(res["out"], want, "bf16")
 

@@ -90,18 +90,13 @@ def test_probe_selection_c4_sampled_rows():
                   | {(0, nb - 1), (31, nb - 1), (5, 0)})
     sc = 1.0 / math.sqrt(d)
     bad = 0
+    kh = lay.k.float().cpu().numpy()
     for h, i in rows:
-        qbar = O.pool(lay.q[i * B:(i + 1) * B, h:h + 1].float().cpu().numpy(), B)[:, :1]  # [1, 1, d]
-        kt = lay.k[: (i + 1) * B, h // G: h // G + 1].float().cpu().numpy()
-        tok = (qbar.reshape(d).astype(np.float32) @ kt[:, 0].T.astype(np.float32)) * np.float32(sc)
-        srow = tok.reshape(i + 1, B).max(axis=1).astype(np.float32)
-        m = srow.max()
+        qbar = O.pool(lay.q[i * B:(i + 1) * B, h:h + 1].float().cpu().numpy(), B)[0, 0]
+        kept, m, srow, amb = P.probe_select_rows(qbar[None], kh, [(h, i)], B, 0.1, sc, G)[0]
         assert abs(rmax[h, i] - m) <= 1e-5 * max(1.0, abs(float(m)))
-        T = float(m) + float(np.float32(math.log(0.1)))
-        keep = (srow - m).astype(np.float32) >= np.float32(math.log(0.1))
-        keep[i] = True
-        amb = np.abs(srow.astype(np.float64) - T) <= 1e-5 * max(1.0, abs(T), abs(float(m)))
-        amb[i] = False
+        keep = np.zeros(i + 1, bool)
+        keep[kept] = True
         off = h * (nb * (nb + 1) // 2) + i * (i + 1) // 2
         got = np.zeros(i + 1, bool)
         got[idx[off: off + int(counts[h, i])].cpu().numpy()] = True

@@ -351,3 +351,76 @@ def test_prefill_dense_tau_zero_matches_textbook():
     assert all(len(r["lists"][h][i]) == i + 1 for h in range(Hq) for i in range(4))
     np.testing.assert_allclose(r["out"], O.dense_causal_attention(q, k, v, 1 / math.sqrt(d)),
                                atol=1e-12)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.1, 1.0])
+def test_select_rows_equals_whole_layer_selection(tau):
+    """select_rows (selection of sampled rows, used where a layer is too large
+    to score whole) is pinned to the whole-layer chain pool -> block_scores ->
+    select -> ambiguous: for every (h, i) of structured GQA layers with a
+    ragged last block, the same row max, the same scores and the same kept set
+    outside the tie zone.  Two kv groups with different structure, so a wrong
+    head-to-group map changes the selection; rows whose lists reach their
+    diagonal, so a wrong slice bound changes it too."""
+    from block_sparse_long_04_amd.inputs import CONFIGS, make_layer
+    for Hq, Hkv, L in ((8, 2, 1000), (8, 4, 1300), (6, 2, 777)):
+        cfg = CONFIGS["c2"].with_(seq_len=L, num_q_heads=Hq, num_kv_heads=Hkv)
+        lay = make_layer(cfg)
+        q, k = lay.q32.numpy(), lay.k32.numpy()
+        B, G, sc = cfg.block_size, Hq // Hkv, 1.0 / math.sqrt(cfg.head_dim)
+        qbar, kbar = O.pool(q, B), O.pool(k, B)
+        S = O.block_scores(qbar, kbar, sc)
+        keep, m = O.select(S, tau)
+        amb = O.ambiguous(S, m, tau)
+        # the row's tie zone must be the whole-layer one up to the rounding of
+        # its scores: between the zones of half and twice the tolerance
+        amb_lo = O.ambiguous(S, m, tau, rel=0.5e-5)
+        amb_hi = O.ambiguous(S, m, tau, rel=2e-5)
+        nb = qbar.shape[1]
+        rows = [(h, i) for h in range(Hq) for i in range(nb)]
+        res = O.select_rows(qbar[[h for h, _ in rows], [i for _, i in rows]], kbar, rows, tau, sc, G)
+        n_kept_off_diag = 0
+        for (h, i), (kept, mr, srow, amb_r) in zip(rows, res):
+            assert abs(float(mr) - float(m[h, i])) <= 1e-6 * max(1.0, abs(float(m[h, i])))
+            np.testing.assert_allclose(srow, S[h, i, : i + 1], rtol=1e-6, atol=1e-6)
+            assert srow.shape == (i + 1,) and amb_r.shape == (i + 1,)
+            got = np.zeros(i + 1, bool)
+            got[kept] = True
+            free = ~(amb[h, i, : i + 1] | amb_r)
+            assert np.array_equal(got[free], keep[h, i, : i + 1][free]), (h, i)
+            assert got[i] and not amb_r[i]
+            assert not (amb_lo[h, i, : i + 1] & ~amb_r).any(), (h, i)
+            assert not (amb_r & ~amb_hi[h, i, : i + 1]).any(), (h, i)
+            n_kept_off_diag += int(got[:i].sum())
+        # the layers select non-trivially (not only the diagonal, not all)
+        if tau == 0.1:
+            total = sum(i for _, i in rows)
+            assert 0 < n_kept_off_diag < total
+
+
+def test_select_rows_tie_zone_hand_built():
+    """Hand-placed scores around the threshold T = m + ln(0.1): pooled keys
+    are unit vectors, so S[i, j] = Qbar[i, j] exactly (sm_scale 1).  With
+    m = 2.5 the zone half-width is 1e-5 * |m| = 2.5e-5, wider than the floor
+    1e-5, so a block 1.8e-5 above T is ambiguous only through the |m| term; a
+    block at T (to fp32 rounding) is ambiguous; blocks 1e-3 either side are
+    decided.  select_rows must give the whole-layer tie zone and decisions."""
+    nb, d = 6, 8
+    lt = float(O.ln_tau(0.1))
+    m = 2.5
+    T = m + lt
+    row = np.array([m, T + 1.8e-5, T, T + 1e-3, T - 1e-3, 0.0], np.float32)
+    qbar = np.zeros((1, nb, d), np.float32)
+    qbar[0, nb - 1, :nb] = row
+    kbar = np.zeros((1, nb, d), np.float32)
+    kbar[0, np.arange(nb), np.arange(nb)] = 1.0
+    S = O.block_scores(qbar, kbar, 1.0)
+    keep, mm = O.select(S, 0.1)
+    amb = O.ambiguous(S, mm, 0.1)
+    i = nb - 1
+    assert amb[0, i].tolist() == [False, True, True, False, False, False]
+    kept, mr, srow, amb_r = O.select_rows(qbar[:, i], kbar, [(0, i)], 0.1, 1.0, 1)[0]
+    assert float(mr) == float(mm[0, i]) == np.float32(m)
+    assert amb_r.tolist() == amb[0, i].tolist()
+    assert kept.tolist() == np.flatnonzero(keep[0, i]).tolist()
+    assert set(kept.tolist()) >= {0, 3, i} and 4 not in kept.tolist()

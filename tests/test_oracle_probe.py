@@ -74,3 +74,36 @@ def test_single_token_spike_is_kept_by_the_probe_only():
     # falls below max + ln 0.1; probe: block 2 sets the max, block 5 stays
     assert probe["lists"][0][last].tolist() == [2, 5, last]
     assert pooled["lists"][0][last].tolist() == [5, last]
+
+
+def test_probe_select_rows_equals_whole_layer():
+    """probe_select_rows (sampled rows of large layers) against select_probe
+    on whole structured GQA layers with a ragged last block: same row max,
+    scores, tie zone and kept set for every (h, i)."""
+    from block_sparse_long_04_amd.inputs import CONFIGS, make_layer
+    for Hq, Hkv, L in ((8, 2, 1000), (4, 4, 1300)):
+        cfg = CONFIGS["c2"].with_(seq_len=L, num_q_heads=Hq, num_kv_heads=Hkv)
+        lay = make_layer(cfg)
+        q, k = lay.q32.numpy(), lay.k32.numpy()
+        B, G, sc = cfg.block_size, Hq // Hkv, 1.0 / math.sqrt(cfg.head_dim)
+        for tau in (0.1, 1.0):
+            ref = P.select_probe(q, k, B, tau, sc)
+            nb = ref["qbar"].shape[1]
+            rows = [(h, i) for h in range(Hq) for i in range(nb)]
+            qr = ref["qbar"][[h for h, _ in rows], [i for _, i in rows]]
+            res = P.probe_select_rows(qr, k, rows, B, tau, sc, G)
+            # a row's scores come from a matrix-vector product, the layer's
+            # from a matrix product: equal to fp32 rounding, so the tie zone
+            # lies between the whole-layer zones of half and twice the width
+            lo = O.ambiguous(ref["S"], ref["row_max"], tau, rel=0.5e-5)
+            hi = O.ambiguous(ref["S"], ref["row_max"], tau, rel=2e-5)
+            for (h, i), (kept, m, srow, amb) in zip(rows, res):
+                m0 = float(ref["row_max"][h, i])
+                assert abs(float(m) - m0) <= 1e-6 * max(1.0, abs(m0))
+                np.testing.assert_allclose(srow, ref["S"][h, i, : i + 1], rtol=1e-6, atol=1e-6)
+                assert not (lo[h, i, : i + 1] & ~amb).any() and not (amb & ~hi[h, i, : i + 1]).any()
+                got = np.zeros(i + 1, bool)
+                got[kept] = True
+                free = ~(amb | ref["amb"][h, i, : i + 1])
+                assert np.array_equal(got[free], ref["keep"][h, i, : i + 1][free]), (h, i)
+                assert got[i]
