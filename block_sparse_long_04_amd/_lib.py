@@ -18,14 +18,15 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libflashprefill.so")
 
 FP_F32, FP_BF16, FP_FP8_E4M3 = 0, 1, 2
-FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP = 0, -1, -2, -3, -4
+FP_OK, FP_ERR_INVALID, FP_ERR_UNSUPPORTED, FP_ERR_WORKSPACE, FP_ERR_HIP, FP_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+FP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 FP_SELECT_TOPK, FP_SELECT_TOPP = 1, 2
 
 EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_group",
             "fp_block_select_sorted",
             "fp_block_select_probe", "fp_sparse_prefill", "fp_workspace_layout_varlen", "fp_block_pool_varlen",
-            "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_strerror")
+            "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_prefill_noalloc", "fp_strerror")
 
 
 class FpProblem(ctypes.Structure):
@@ -99,6 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [P, VL, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.fp_prefill_noalloc.argtypes = [P, ctypes.c_void_p]
+    lib.fp_prefill_noalloc.restype = ctypes.c_int
     lib.fp_strerror.argtypes = [ctypes.c_int]
     lib.fp_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -154,6 +157,10 @@ def fp_block_select_probe(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: i
 def fp_sparse_prefill(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check(load_library().fp_sparse_prefill(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
            "fp_sparse_prefill")
+
+
+def fp_prefill_noalloc(prob: FpProblem, stream: int) -> None:
+    _check(load_library().fp_prefill_noalloc(ctypes.byref(prob), stream), "fp_prefill_noalloc")
 
 
 def fp_workspace_layout_varlen(prob: FpProblem, vl: FpVarlen) -> FpWsLayoutVarlen:

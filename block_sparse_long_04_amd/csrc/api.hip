@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "varlen.h"
 
@@ -185,7 +187,57 @@ int check_ws_varlen(const fp_problem* p, const fp_varlen* vl, FpDims* dm, VlInfo
 
 }  // namespace
 
+// ---- fixed scratch buffer of fp_prefill_noalloc -----------------------------
+// The workspace of callers that cannot allocate.  Each GPU the library's code
+// is loaded on holds its own copy at its own address; host code never uses
+// the array's name as an address (it names a host-side stand-in), only the
+// per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[FP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, queried once per device
+// with that device current.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FP_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+int fp_prefill_noalloc(const fp_problem* p, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (dm.L == 0) return FP_OK;
+  if (!p->q || !p->k || !p->v || !p->out || !aligned16(p->q) || !aligned16(p->k) ||
+      !aligned16(p->v) || !aligned16(p->out))
+    return FP_ERR_INVALID;
+  fp_ws_layout w;
+  layout_of(p, dm, &w);
+  if (w.total > FP_NOALLOC_SCRATCH_BYTES) return FP_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_on_current_device(&ws);
+  if (rc != FP_OK) return rc;
+  rc = fp_block_pool(p, ws, FP_NOALLOC_SCRATCH_BYTES, stream);
+  if (rc == FP_OK) rc = fp_block_select(p, ws, FP_NOALLOC_SCRATCH_BYTES, stream);
+  if (rc == FP_OK) rc = fp_sparse_prefill(p, ws, FP_NOALLOC_SCRATCH_BYTES, stream);
+  return rc;
+}
 
 int fp_workspace_layout(const fp_problem* p, fp_ws_layout* layout) {
   FpDims dm;
@@ -387,6 +439,7 @@ const char* fp_strerror(int code) {
     case FP_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, block_size, causal or block count)";
     case FP_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FP_ERR_HIP: return "HIP launch failed";
+    case FP_ERR_SCRATCH: return "problem too large for the library's fixed scratch buffer (fp_prefill_noalloc)";
     default: return "unknown error code";
   }
 }

@@ -63,7 +63,8 @@ enum {
   FP_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size not 64/128, causal != 1,
                               more than 16384 blocks */
   FP_ERR_WORKSPACE = -3,   /* workspace null, misaligned (256 B) or smaller than fp_workspace_layout().total */
-  FP_ERR_HIP = -4          /* the HIP runtime refused a launch */
+  FP_ERR_HIP = -4,         /* the HIP runtime refused a launch */
+  FP_ERR_SCRATCH = -5      /* fp_prefill_noalloc: the problem's workspace exceeds FP_NOALLOC_SCRATCH_BYTES */
 };
 
 /* One layer's prefill problem (batch 1). */
@@ -227,6 +228,25 @@ int fp_block_select_varlen(const fp_problem* p, const fp_varlen* vl, void* works
  * the same workspace. */
 int fp_sparse_prefill_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): steps 1-5
+ * of one layer -- fp_block_pool, fp_block_select and fp_sparse_prefill, the
+ * same kernels and results -- with the workspace held in a buffer of
+ * FP_NOALLOC_SCRATCH_BYTES that the library itself keeps in device memory (one
+ * per GPU, created when the library's code is loaded on that GPU and held until
+ * the process ends).  The caller passes q, k, v and out as for the three
+ * calls; nothing is allocated or freed, and the selection stays inside the
+ * library (it cannot be read or injected).  Problems whose
+ * fp_workspace_layout().total exceeds FP_NOALLOC_SCRATCH_BYTES are rejected
+ * with FP_ERR_SCRATCH before any launch (at 32 query / 8 kv heads, head_dim
+ * and block_size 128, that allows sequences up to 28672 tokens).  Every call on
+ * one GPU uses that GPU's one buffer: calls that overlap in time on a GPU
+ * (other streams, other host threads) race and must be ordered by the caller.
+ * No part of the buffer needs to start at zero: each call writes every section
+ * before it reads it. */
+#define FP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fp_prefill_noalloc(const fp_problem* p, void* stream);
 
 /* Static, human-readable text of a return code. */
 const char* fp_strerror(int code);

@@ -351,3 +351,21 @@ def test_list_validation_rejects_bad_lists_before_any_write():
     ws.set_lists(counts, idx)
     assert np.array_equal(ws.counts().numpy(), counts)
     assert np.array_equal(ws.indices().numpy(), idx)
+
+
+def test_noalloc_rejects_problems_larger_than_its_buffer_before_any_gpu_call():
+    """fp_prefill_noalloc checks the problem and its workspace size against
+    the fixed scratch buffer on the host first: a 32K-token, 32 / 8-head
+    layer needs more and is refused with FP_ERR_SCRATCH, and a bad problem
+    with FP_ERR_INVALID, without touching a GPU (none is visible here)."""
+    p = prob(seq_len=32768, num_q_heads=32, num_kv_heads=8)
+    assert _lib.fp_workspace_layout(p).total > _lib.FP_NOALLOC_SCRATCH_BYTES
+    p.q = p.k = p.v = p.out = 1 << 20  # aligned, non-null: only the size check refuses
+    with pytest.raises(_lib.FlashPrefillError) as e:
+        _lib.fp_prefill_noalloc(p, 0)
+    assert e.value.code == _lib.FP_ERR_SCRATCH
+    small = prob(seq_len=4096, num_q_heads=32, num_kv_heads=8)
+    assert _lib.fp_workspace_layout(small).total <= _lib.FP_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(_lib.FlashPrefillError) as e:  # null pointers
+        _lib.fp_prefill_noalloc(small, 0)
+    assert e.value.code == _lib.FP_ERR_INVALID
