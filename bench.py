@@ -2,8 +2,9 @@
 """Block-sparse causal prefill benchmark on one MI355X.
 
 One step = one layer's whole hot path through the C ABI:
-fp_block_pool (pool Q/K, V^T layout) -> fp_block_select (scores, max
-threshold, lists) -> fp_sparse_prefill (attention over the kept blocks), on
+fp_block_pool (pool Q/K) -> fp_block_select (scores, max threshold, lists)
+-> fp_sparse_prefill (V^T layout pass, then attention over the kept
+blocks), on
 seeded synthetic inputs already resident in HBM.  The default workload is the
 Llama-3-8B-shaped layer at L = 131072 (32 q / 8 kv heads, d = 128, B = 128,
 bf16, tau = 0.1).
@@ -57,6 +58,11 @@ def parse():
                          "union list per kv group (fp_block_select_group)")
     ap.add_argument("--no-group", action="store_true",
                     help="skip the group-shared selection measurement")
+    ap.add_argument("--attention", choices=("default", "pack"), default="default",
+                    help="attention of the timed step: fp_sparse_prefill, or fp_sparse_prefill_pack "
+                         "(two query heads per workgroup; bf16 with an even group size)")
+    ap.add_argument("--no-pack", action="store_true",
+                    help="skip the two-heads-per-workgroup attention measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -101,11 +107,17 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-ATTN_SOURCES = ["block_sparse_long_04_amd/csrc/attn_mfma.hip",
-                "block_sparse_long_04_amd/csrc/common.h"]
+ATTN_SOURCES = {
+    "default": ["block_sparse_long_04_amd/csrc/attn_mfma.hip",
+                "block_sparse_long_04_amd/csrc/attn_common.h",
+                "block_sparse_long_04_amd/csrc/common.h"],
+    "pack": ["block_sparse_long_04_amd/csrc/attn_pack.hip",
+             "block_sparse_long_04_amd/csrc/attn_common.h",
+             "block_sparse_long_04_amd/csrc/common.h"],
+}
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, attention: str = "default"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary, only if it was taken on the current attention source."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
@@ -115,7 +127,7 @@ def measured_traffic(workload: str):
         rec = json.load(open(path)).get(workload)
     except Exception:
         return None
-    if not rec or rec.get("source_hash") != source_hash(ATTN_SOURCES):
+    if not rec or rec.get("source_hash") != source_hash(ATTN_SOURCES[attention]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -259,6 +271,28 @@ def select_baselines(pf, _lib, torch, thr_ms, k, p, reps=5):
     return out
 
 
+def pack_attention(pf, torch, flops, attn_ms, reps=5):
+    """fp_sparse_prefill_pack on the step's own lists (median of `reps`
+    runs), against the step's fp_sparse_prefill time; the outputs of the two
+    are bit-identical (checked here too)."""
+    pf.attend()
+    ref = pf.out.clone()
+    pf.attend_pack()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref, pf.out))
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pf.attend_pack()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[reps // 2]
+    return {"attention_ms": round(ms, 4), "attention_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "vs_default_attention": round(ms / attn_ms, 3), "bit_identical_to_default": same}
+
+
 def group_select(pf, torch, kept_pairs, cfg, per_head, reps=5):
     """Group-shared selection (fp_block_select_group: each head's own
     threshold, then one union list per kv group) and the attention on its
@@ -366,6 +400,7 @@ def main():
     layer.out = pf.out
 
     select = pf.select_group if args.select == "group" else pf.select
+    attend = pf.attend_pack if args.attention == "pack" else pf.attend
 
     def step(ev=None):
         if ev is not None:
@@ -376,7 +411,7 @@ def main():
         select()
         if ev is not None:
             ev[2].record()
-        pf.attend()
+        attend()
         if ev is not None:
             ev[3].record()
 
@@ -413,17 +448,18 @@ def main():
     flops = 4.0 * d * pairs
     density = float(counts.sum()) / (Hq * nb * (nb + 1) / 2)
     esz = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.dtype]
-    mfma_path = cfg.dtype in ("bf16", "fp8") and d == 128 and B == 128  # V^T pass in pool
-    pool_bytes = (L * (Hq + Hkv) * d * esz + (Hq + Hkv) * nb * d * 4
-                  + ((L * Hkv * d * esz + Hkv * d * nb * B * 2) if mfma_path else 0))
+    mfma_path = cfg.dtype in ("bf16", "fp8") and d == 128 and B == 128
+    # algorithmic bytes of step 1: Q and K read once, the pooled proxies written
+    pool_bytes = L * (Hq + Hkv) * d * esz + (Hq + Hkv) * nb * d * 4
     sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2
     attn_tflops = flops / (stage_ms["attention"] * 1e-3) / 1e12
     # matrix-core attention for bf16 / e4m3 with d = B = 128; otherwise the
     # generic kernel, fp32 vector ALUs
     bound = "mfma" if mfma_path else "alu"
     peak = PEAK["fp8"] if cfg.dtype == "fp8" else (PEAK["bf16"] if mfma_path else PEAK["fp32"])
-    wl = cfg.name + f"_tau{tau:g}" + ("_group" if args.select == "group" else "")
-    traffic = measured_traffic(wl)
+    wl = (cfg.name + f"_tau{tau:g}" + ("_group" if args.select == "group" else "")
+          + ("_pack" if args.attention == "pack" else ""))
+    traffic = measured_traffic(wl, args.attention)
     res = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -455,9 +491,12 @@ def main():
         "pool_hbm_frac": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK["hbm_gbs"], 4),
         "select_tflops_fp32": round(sel_flops / (stage_ms["select"] * 1e-3) / 1e12, 2),
         "select_fp32_frac": round(sel_flops / (stage_ms["select"] * 1e-3) / 1e12 / PEAK["fp32"], 4),
+        # the attention stage's events also hold its V^T layout pass (matrix-core
+        # path), so "achieved" slightly understates the attention kernel alone
         "roofline": {"bound": bound, "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": traffic},
+        "attention_stage_includes_vt_pass": bool(mfma_path),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and args.select == "threshold":  # its sample checks per-head lists
@@ -477,6 +516,11 @@ def main():
         k_match = max(1, int(round(float(counts.mean()))))
         res["select_baselines"] = select_baselines(pf, _lib, torch, stage_ms["select"], k_match, 0.9)
         select()  # leave the step's lists in the workspace
+    if (not args.no_pack and args.attention == "default" and cfg.dtype == "bf16" and mfma_path
+            and (Hq // Hkv) % 2 == 0):
+        # the same lists attended with two query heads per workgroup
+        print("[bench] two-heads-per-workgroup attention", file=sys.stderr, flush=True)
+        res["pack_attention"] = pack_attention(pf, torch, flops, stage_ms["attention"])
     if not args.no_group and args.select == "threshold" and Hq > Hkv and tau > 0:
         # one list per kv group (the union of its heads' selections)
         print("[bench] group-shared selection", file=sys.stderr, flush=True)

@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     fp_sparse_prefill, fp_workspace_layout, load_library, make_problem, prefill, strerror,
     FpVarlen, FpWsLayoutVarlen, PrefillVarlen, fp_block_pool_varlen, fp_block_select_varlen,
     fp_sparse_prefill_varlen, fp_workspace_layout_varlen, FP_ERR_SCRATCH, FP_NOALLOC_SCRATCH_BYTES,
-    fp_prefill_noalloc, validate_lists,
+    fp_prefill_noalloc, validate_lists, fp_sparse_prefill_pack,
 )

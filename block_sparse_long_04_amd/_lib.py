@@ -26,7 +26,8 @@ FP_SELECT_TOPK, FP_SELECT_TOPP = 1, 2
 EXPORTED = ("fp_workspace_layout", "fp_block_pool", "fp_block_select", "fp_block_select_group",
             "fp_block_select_sorted",
             "fp_block_select_probe", "fp_sparse_prefill", "fp_workspace_layout_varlen", "fp_block_pool_varlen",
-            "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_prefill_noalloc", "fp_strerror")
+            "fp_block_select_varlen", "fp_sparse_prefill_varlen", "fp_prefill_noalloc",
+            "fp_sparse_prefill_pack", "fp_strerror")
 
 
 class FpProblem(ctypes.Structure):
@@ -86,7 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_workspace_layout.argtypes = [P, W]
     lib.fp_workspace_layout.restype = ctypes.c_int
     for name in ("fp_block_pool", "fp_block_select", "fp_block_select_group", "fp_block_select_probe",
-                 "fp_sparse_prefill"):
+                 "fp_sparse_prefill", "fp_sparse_prefill_pack"):
         fn = getattr(lib, name)
         fn.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -157,6 +158,11 @@ def fp_block_select_probe(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: i
 def fp_sparse_prefill(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
     _check(load_library().fp_sparse_prefill(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
            "fp_sparse_prefill")
+
+
+def fp_sparse_prefill_pack(prob: FpProblem, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().fp_sparse_prefill_pack(ctypes.byref(prob), ws_ptr, ws_bytes, stream),
+           "fp_sparse_prefill_pack")
 
 
 def fp_prefill_noalloc(prob: FpProblem, stream: int) -> None:
@@ -393,6 +399,10 @@ class Prefill:
 
     def attend(self):
         fp_sparse_prefill(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
+
+    def attend_pack(self):
+        """Attention with two query heads per workgroup (fp_sparse_prefill_pack)."""
+        fp_sparse_prefill_pack(self.prob, self.ws.ptr, self.ws.nbytes, self.stream())
 
     def run(self):
         self.pool()

@@ -254,14 +254,11 @@ int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, 
   if (rc != FP_OK) return rc;
   if (dm.L == 0) return FP_OK;
   if (!p->q || !p->k || !aligned16(p->q) || !aligned16(p->k)) return FP_ERR_INVALID;
-  if (use_mfma(p, dm) && (!p->v || !aligned16(p->v))) return FP_ERR_INVALID;
   fp_ws_layout w;
   rc = check_ws(p, dm, workspace, workspace_bytes, &w);
   if (rc != FP_OK) return rc;
-  const hipStream_t st = (hipStream_t)stream;
-  hipError_t e = fpk_launch_pool(*p, dm, at<float>(workspace, w.q_pool),
-                                 at<float>(workspace, w.k_pool), st);
-  if (e == hipSuccess && use_mfma(p, dm)) e = fpk_launch_vtrans(*p, dm, at<uint16_t>(workspace, w.v_t), st);
+  const hipError_t e = fpk_launch_pool(*p, dm, at<float>(workspace, w.q_pool), at<float>(workspace, w.k_pool),
+                                       (hipStream_t)stream);
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 
@@ -360,10 +357,35 @@ int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_byt
   const int* indices = at<int>(workspace, w.indices);
   hipError_t e;
   if (use_mfma(p, dm)) {
-    e = fpk_launch_attn_mfma(*p, dm, counts, indices, at<uint16_t>(workspace, w.v_t), sc, st);
+    // V^T is this call's own scratch: written here from v, then read by the
+    // attention (key-contiguous rows for the P.V operands)
+    uint16_t* v_t = at<uint16_t>(workspace, w.v_t);
+    e = fpk_launch_vtrans(*p, dm, v_t, st);
+    if (e == hipSuccess) e = fpk_launch_attn_mfma(*p, dm, counts, indices, v_t, sc, st);
   } else {
     e = fpk_launch_attn_generic(*p, dm, counts, indices, sc, st);
   }
+  return e == hipSuccess ? FP_OK : FP_ERR_HIP;
+}
+
+int fp_sparse_prefill_pack(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+  FpDims dm;
+  int rc = check_problem(p, &dm);
+  if (rc != FP_OK) return rc;
+  if (p->dtype != FP_BF16 || !use_mfma(p, dm) || (dm.Hq / dm.Hkv) % 2 != 0) return FP_ERR_UNSUPPORTED;
+  if (dm.L == 0) return FP_OK;
+  if (!p->q || !p->k || !p->v || !p->out || !aligned16(p->q) || !aligned16(p->k) ||
+      !aligned16(p->v) || !aligned16(p->out))
+    return FP_ERR_INVALID;
+  fp_ws_layout w;
+  rc = check_ws(p, dm, workspace, workspace_bytes, &w);
+  if (rc != FP_OK) return rc;
+  const hipStream_t st = (hipStream_t)stream;
+  uint16_t* v_t = at<uint16_t>(workspace, w.v_t);
+  hipError_t e = fpk_launch_vtrans(*p, dm, v_t, st);
+  if (e == hipSuccess)
+    e = fpk_launch_attn_pack(*p, dm, at<int>(workspace, w.counts), at<int>(workspace, w.indices), v_t,
+                             eff_sm_scale(p), st);
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 
@@ -387,14 +409,11 @@ int fp_block_pool_varlen(const fp_problem* p, const fp_varlen* vl, void* workspa
   int rc = check_ws_varlen(p, vl, &dm, &vi, workspace, workspace_bytes, &w);
   if (rc != FP_OK) return rc;
   if (vi.NB == 0) return FP_OK;
-  if (!p->q || !p->k || !p->v || !aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) ||
-      !vl->cu_seqlens_dev)
-    return FP_ERR_INVALID;
+  if (!p->q || !p->k || !aligned16(p->q) || !aligned16(p->k) || !vl->cu_seqlens_dev) return FP_ERR_INVALID;
   const hipError_t e = fpk_launch_varlen_prepare(
       *p, *vl, dm, vi.NB, at<fpk::VlBlock>(workspace, w.meta),
       reinterpret_cast<fpk::VlSeq*>(at<fpk::VlBlock>(workspace, w.meta) + vi.NB), at<float>(workspace, w.q_pool),
-      at<float>(workspace, w.k_pool), at<uint8_t>(workspace, w.k_c), at<uint16_t>(workspace, w.v_t),
-      (hipStream_t)stream);
+      at<float>(workspace, w.k_pool), at<uint8_t>(workspace, w.k_c), (hipStream_t)stream);
   return e == hipSuccess ? FP_OK : FP_ERR_HIP;
 }
 
@@ -423,9 +442,13 @@ int fp_sparse_prefill_varlen(const fp_problem* p, const fp_varlen* vl, void* wor
   int rc = check_ws_varlen(p, vl, &dm, &vi, workspace, workspace_bytes, &w);
   if (rc != FP_OK) return rc;
   if (vi.NB == 0) return FP_OK;
-  if (!p->q || !p->out || !aligned16(p->q) || !aligned16(p->out)) return FP_ERR_INVALID;
+  if (!p->q || !p->v || !p->out || !aligned16(p->q) || !aligned16(p->v) || !aligned16(p->out))
+    return FP_ERR_INVALID;
   const fpk::VlBlock* blk = at<fpk::VlBlock>(workspace, w.meta);
-  const hipError_t e = fpk_launch_attn_mfma_varlen(
+  // V^T of the batch (this call's own scratch), from packed or paged v
+  hipError_t e = fpk_launch_vtrans_varlen(*p, *vl, dm, vi.NB, blk, at<uint16_t>(workspace, w.v_t),
+                                          (hipStream_t)stream);
+  if (e == hipSuccess) e = fpk_launch_attn_mfma_varlen(
       *p, dm, vi.NB, blk, reinterpret_cast<const fpk::VlSeq*>(blk + vi.NB), at<int>(workspace, w.counts),
       at<int>(workspace, w.indices), at<uint8_t>(workspace, w.k_c), at<uint16_t>(workspace, w.v_t),
       eff_sm_scale(p), (hipStream_t)stream);

@@ -85,5 +85,9 @@ hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int
                                 const int* indices, const uint16_t* v_t, float sm_scale,
                                 hipStream_t st);
 
+// Two query heads of one kv group per wave (bf16, d = B = 128, Hq/Hkv even).
+hipError_t fpk_launch_attn_pack(const fp_problem& p, const FpDims& dm, const int* counts, const int* indices,
+                                const uint16_t* v_t, float sm_scale, hipStream_t st);
+
 hipError_t fpk_launch_attn_generic(const fp_problem& p, const FpDims& dm, const int* counts,
                                    const int* indices, float sm_scale, hipStream_t st);

@@ -24,7 +24,12 @@ struct VlSeq {
 
 hipError_t fpk_launch_varlen_prepare(const fp_problem& p, const fp_varlen& vl, const FpDims& dm, int NB,
                                      fpk::VlBlock* blk, fpk::VlSeq* seq, float* q_pool, float* k_pool,
-                                     uint8_t* k_c, uint16_t* v_t, hipStream_t st);
+                                     uint8_t* k_c, hipStream_t st);
+
+// V^T [Hkv][d][NB * B] (bf16; e4m3 codes widened) of the batch, zero past
+// each sequence's end, from packed or paged v.
+hipError_t fpk_launch_vtrans_varlen(const fp_problem& p, const fp_varlen& vl, const FpDims& dm, int NB,
+                                    const fpk::VlBlock* blk, uint16_t* v_t, hipStream_t st);
 
 hipError_t fpk_launch_select_varlen(const FpDims& dm, int NB, const fpk::VlBlock* blk, const fpk::VlSeq* seq,
                                     const float* q_pool, const float* k_pool, float sm_scale, float ln_tau,

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void select_varlen_kernel(const float* __restr
 
 hipError_t fpk_launch_varlen_prepare(const fp_problem& p, const fp_varlen& vl, const FpDims& dm, int NB,
                                      fpk::VlBlock* blk, fpk::VlSeq* seq, float* q_pool, float* k_pool,
-                                     uint8_t* k_c, uint16_t* v_t, hipStream_t st) {
+                                     uint8_t* k_c, hipStream_t st) {
   hipLaunchKernelGGL(varlen_meta_kernel, dim3(1), dim3(256), 0, st, vl.cu_seqlens_dev, vl.num_seqs, dm.B, dm.Hq,
                      NB, blk, seq);
   const bool fp8 = p.dtype == FP_FP8_E4M3;
@@ -392,23 +392,29 @@ hipError_t fpk_launch_varlen_prepare(const fp_problem& p, const fp_varlen& vl, c
   VlSrc qs{static_cast<const uint8_t*>(p.q), p.q_stride_tok, p.q_stride_head, 0, nullptr, 0, 0};
   VlSrc ks{static_cast<const uint8_t*>(p.k), p.k_stride_tok, p.k_stride_head, vl.k_page_stride, table,
            vl.max_blocks, vl.num_pages};
-  VlSrc vs{static_cast<const uint8_t*>(p.v), p.v_stride_tok, p.v_stride_head, vl.v_page_stride, table,
-           vl.max_blocks, vl.num_pages};
   const int wgq = (dm.Hq * dm.d / vec + 63) / 64;
   const int wgk = (dm.Hkv * dm.d / vec + 63) / 64;
   const dim3 gp((unsigned)(NB * (wgq + wgk)));
   const float qsc = fp8 ? p.q_scale : 1.f, ksc = fp8 ? p.k_scale : 1.f;
-  const int Lpad = NB * dm.B;
-  const dim3 gv((unsigned)(Lpad / 64), (unsigned)(dm.d / 64), (unsigned)dm.Hkv);
-  if (fp8) {
+  if (fp8)
     hipLaunchKernelGGL(pool_varlen_kernel<1>, gp, dim3(256), 0, st, qs, ks, blk, q_pool, k_pool, k_c, dm.Hq, dm.Hkv,
                        dm.d, dm.B, NB, qsc, ksc, wgq, wgk);
-    hipLaunchKernelGGL(vtrans_varlen_kernel<1>, gv, dim3(256), 0, st, vs, blk, dm.d, dm.B, Lpad, v_t);
-  } else {
+  else
     hipLaunchKernelGGL(pool_varlen_kernel<2>, gp, dim3(256), 0, st, qs, ks, blk, q_pool, k_pool, k_c, dm.Hq, dm.Hkv,
                        dm.d, dm.B, NB, qsc, ksc, wgq, wgk);
+  return hipGetLastError();
+}
+
+hipError_t fpk_launch_vtrans_varlen(const fp_problem& p, const fp_varlen& vl, const FpDims& dm, int NB,
+                                    const fpk::VlBlock* blk, uint16_t* v_t, hipStream_t st) {
+  VlSrc vs{static_cast<const uint8_t*>(p.v), p.v_stride_tok, p.v_stride_head, vl.v_page_stride, vl.block_table_dev,
+           vl.max_blocks, vl.num_pages};
+  const int Lpad = NB * dm.B;
+  const dim3 gv((unsigned)(Lpad / 64), (unsigned)(dm.d / 64), (unsigned)dm.Hkv);
+  if (p.dtype == FP_FP8_E4M3)
+    hipLaunchKernelGGL(vtrans_varlen_kernel<1>, gv, dim3(256), 0, st, vs, blk, dm.d, dm.B, Lpad, v_t);
+  else
     hipLaunchKernelGGL(vtrans_varlen_kernel<2>, gv, dim3(256), 0, st, vs, blk, dm.d, dm.B, Lpad, v_t);
-  }
   return hipGetLastError();
 }
 

@@ -97,10 +97,10 @@ typedef struct fp_problem {
  *   counts  int32 [num_q_heads][nb]             kept blocks of row (h,i)
  *   indices int32, triangular: row (h,i) starts at h*nb*(nb+1)/2 + i*(i+1)/2, holds
  *           counts[h][i] ascending key-block indices (capacity i+1)
- *   v_t     bf16 [num_kv_heads][head_dim][nb*block_size]  V transposed per kv head, zero past
- *           seq_len; e4m3 codes are widened to bf16 exactly, v_scale is applied at the output
- *           (written by fp_block_pool; zero-length unless the input is bf16 or e4m3 with
- *           head_dim 128 and block_size 128)
+ *   v_t     bf16 [num_kv_heads][head_dim][nb*block_size]  scratch of fp_sparse_prefill: V
+ *           transposed per kv head (the key-contiguous rows its P.V products read), zero past
+ *           seq_len; e4m3 codes widened to bf16 exactly, v_scale applied at the output
+ *           (zero-length unless the input is bf16 or e4m3 with head_dim 128 and block_size 128)
  * The layout is part of the ABI: a caller may read the selection, or write
  * its own counts/indices (ascending, each list ending with its diagonal
  * block i) before fp_sparse_prefill to run attention on a given mask. */
@@ -112,11 +112,7 @@ typedef struct fp_ws_layout {
  * fills *layout.  Returns FP_OK or an error code. */
 int fp_workspace_layout(const fp_problem* p, fp_ws_layout* layout);
 
-/* Step 1.  Reads q and k and writes the q_pool and k_pool sections.  For
- * bf16 or e4m3 inputs with head_dim 128 and block_size 128 it also reads v and
- * writes the v_t section (the key-contiguous V layout the matrix-core attention
- * reads), so that stage streams V once here rather than inside the attention
- * loop. */
+/* Step 1.  Reads q and k and writes the q_pool and k_pool sections. */
 int fp_block_pool(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Steps 2-4.  Reads q_pool, k_pool; writes row_max, counts and indices.  The
@@ -165,9 +161,25 @@ int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* wor
  * (FP_ERR_UNSUPPORTED otherwise). */
 int fp_block_select_probe(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Step 5.  Reads q, k, v (or v_t, written by fp_block_pool), counts and
- * indices; writes out.  Must follow fp_block_pool on the same workspace. */
+/* Step 5.  Reads q, k, v, counts and indices; writes out (and, for bf16 or
+ * e4m3 inputs with head_dim 128 and block_size 128, first the v_t section,
+ * from v, which its attention kernel then reads). */
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 5 with the two query heads of a pair (2p, 2p+1) of one kv group served
+ * by one workgroup (FlashPrefill V2 abstract: PackGQA, the query heads of a kv
+ * group share the K/V tiles they read): each K and V tile is staged into LDS
+ * once for both heads, and every operand fragment read from LDS feeds both
+ * heads' matrix products.  Each head still attends over exactly its own list:
+ * the kernel walks the union of the pair's lists and gives a head zero weight
+ * on a block its own list lacks.  Same inputs, workspace and result as
+ * fp_sparse_prefill (any lists, per-head or group-shared); bf16 inputs with
+ * head_dim 128, block_size 128 and an even num_q_heads / num_kv_heads only
+ * (FP_ERR_UNSUPPORTED otherwise).  It halves the LDS operand reads and the
+ * tile loads of fp_sparse_prefill per product but runs one wave per SIMD
+ * (its registers allow no second), and on MI355X it is slower than
+ * fp_sparse_prefill, which remains the default. */
+int fp_sparse_prefill_pack(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Batches of independent sequences (varlen), K/V packed or paged.
@@ -215,8 +227,8 @@ typedef struct fp_ws_layout_varlen {
  * may be NULL here) and fills *layout. */
 int fp_workspace_layout_varlen(const fp_problem* p, const fp_varlen* vl, fp_ws_layout_varlen* layout);
 
-/* Step 1 of every sequence: block metadata, pooled proxies, gathered K and
- * V^T (reads q, k, v and cu_seqlens_dev / block_table_dev). */
+/* Step 1 of every sequence: block metadata, pooled proxies and gathered K
+ * (reads q, k and cu_seqlens_dev / block_table_dev). */
 int fp_block_pool_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
                          void* stream);
 
@@ -224,8 +236,10 @@ int fp_block_pool_varlen(const fp_problem* p, const fp_varlen* vl, void* workspa
 int fp_block_select_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* Step 5 of every sequence; writes out.  Must follow fp_block_pool_varlen on
- * the same workspace. */
+/* Step 5 of every sequence: V^T of the batch into the v_t section (from v,
+ * packed or paged), then the attention; writes out.  Must follow
+ * fp_block_pool_varlen (block metadata, gathered K) and a selection on the
+ * same workspace. */
 int fp_sparse_prefill_varlen(const fp_problem* p, const fp_varlen* vl, void* workspace, size_t workspace_bytes,
                              void* stream);
 

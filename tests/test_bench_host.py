@@ -49,15 +49,23 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_record_needs_the_current_attention_source(tmp_path, monkeypatch):
-    rec = {"w": {"bytes_per_launch": 123, "source_hash": bench.source_hash(bench.ATTN_SOURCES)},
+    rec = {"w": {"bytes_per_launch": 123, "source_hash": bench.source_hash(bench.ATTN_SOURCES["default"])},
+           "w_pack": {"bytes_per_launch": 77, "source_hash": bench.source_hash(bench.ATTN_SOURCES["pack"])},
            "stale": {"bytes_per_launch": 456, "source_hash": "0" * 16}}
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "attn_traffic.json").write_text(json.dumps(rec))
-    for f in bench.ATTN_SOURCES:
+    for f in set(bench.ATTN_SOURCES["default"]) | set(bench.ATTN_SOURCES["pack"]):
         os.makedirs(tmp_path / os.path.dirname(f), exist_ok=True)
         with open(os.path.join(ROOT, f), "rb") as src, open(tmp_path / f, "wb") as dst:
             dst.write(src.read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic("w") == 123
+    assert bench.measured_traffic("w_pack", "pack") == 77
+    assert bench.measured_traffic("w_pack") is None  # keyed on the other kernel's sources
     assert bench.measured_traffic("stale") is None
     assert bench.measured_traffic("missing") is None
+    # a change to a source of one kernel invalidates that kernel's record only
+    with open(tmp_path / bench.ATTN_SOURCES["pack"][0], "ab") as f:
+        f.write(b"\n")
+    assert bench.measured_traffic("w_pack", "pack") is None
+    assert bench.measured_traffic("w") == 123

@@ -172,6 +172,8 @@ def test_e4m3_decode_of_every_code_in_pool_and_vt():
     q, k, v = q8.to(dev), k8.to(dev), v8.to(dev)
     pf = _lib.Prefill(q, k, v, block_size=B, threshold=0.1, q_scale=1.0, k_scale=1.0, v_scale=1.0)
     pf.pool()
+    pf.select()
+    pf.attend()  # writes its V^T scratch, then attends (NaN codes give NaN outputs; not checked)
     torch.cuda.synchronize()
     want = q8[128].float()  # torch decode, [H, d]
     for got in (pf.ws.k_pool()[:, 1, :].cpu(), pf.ws.q_pool()[:, 1, :].cpu()):
