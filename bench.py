@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--config", default="c4",
                     help="workload key: c1 c2 c3 c4 c4_fp8 c4_dense c5")
     ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="override the workload's head dimension (64 or 128)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="override the workload's block size (64 or 128)")
     ap.add_argument("--evict-mib", type=int, default=512,
                     help="before each timed step, outside its events, read a buffer of this many "
                          "MiB so the Infinity Cache (256 MiB) holds none of the previous step's data "
@@ -254,7 +258,7 @@ def select_baselines(pf, _lib, torch, thr_ms, k, p, reps=5):
         ms = sorted(ts)[reps // 2]
         out[name] = {"param": param, "ms": round(ms, 4), "vs_threshold": round(ms / thr_ms, 2),
                      "kept_blocks": int(pf.ws.counts().sum().item())}
-    if pf.ws.nb <= 1024 and pf.prob.dtype != _lib.FP_F32:
+    if pf.ws.nb <= 1024 and pf.prob.dtype != _lib.FP_F32 and pf.prob.head_dim == 128 and pf.prob.block_size == 128:
         # the query-probe reading of stage 1 (token-level max per key block)
         pf.select_probe()
         ts = []
@@ -392,6 +396,13 @@ def main():
     _lib.load_library()
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.config]
+    over = {}
+    if args.head_dim is not None:
+        over["head_dim"] = args.head_dim
+    if args.block_size is not None:
+        over["block_size"] = args.block_size
+    if over:
+        cfg = cfg.with_(name=cfg.name + "".join(f"_{k[0]}{v}" for k, v in sorted(over.items())), **over)
     tau = cfg.taus[0] if args.tau is None else args.tau
     print(f"[bench] building {cfg.name} on the GPU", file=sys.stderr, flush=True)
     layer = make_layer(cfg, device=dev, keep_fp32=False)
@@ -448,7 +459,8 @@ def main():
     flops = 4.0 * d * pairs
     density = float(counts.sum()) / (Hq * nb * (nb + 1) / 2)
     esz = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.dtype]
-    mfma_path = cfg.dtype in ("bf16", "fp8") and d == 128 and B == 128
+    # matrix cores: bf16 / e4m3 with d = B = 128, or bf16 with d, B in {64, 128}
+    mfma_path = (cfg.dtype in ("bf16", "fp8") and d == 128 and B == 128) or cfg.dtype == "bf16"
     # algorithmic bytes of step 1: Q and K read once, the pooled proxies written
     pool_bytes = L * (Hq + Hkv) * d * esz + (Hq + Hkv) * nb * d * 4
     sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2
@@ -516,7 +528,7 @@ def main():
         k_match = max(1, int(round(float(counts.mean()))))
         res["select_baselines"] = select_baselines(pf, _lib, torch, stage_ms["select"], k_match, 0.9)
         select()  # leave the step's lists in the workspace
-    if (not args.no_pack and args.attention == "default" and cfg.dtype == "bf16" and mfma_path
+    if (not args.no_pack and args.attention == "default" and cfg.dtype == "bf16" and d == 128 and B == 128
             and (Hq // Hkv) % 2 == 0):
         # the same lists attended with two query heads per workgroup
         print("[bench] two-heads-per-workgroup attention", file=sys.stderr, flush=True)

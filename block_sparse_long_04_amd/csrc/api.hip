@@ -81,6 +81,13 @@ bool use_mfma(const fp_problem* p, const FpDims& dm) {
   return (int64_t)dm.B * p->k_stride_tok * esz + dm.d * esz < (int64_t(1) << 31);
 }
 
+// bf16 layers with head_dim or block_size 64 (d, B in {64, 128}) take the
+// matrix-core kernel of attn_small.hip (d = B = 128 takes attn_mfma.hip).
+bool use_small(const fp_problem* p, const FpDims& dm) {
+  if (p->dtype != FP_BF16 || use_mfma(p, dm)) return false;
+  return (dm.d == 64 || dm.d == 128) && (dm.B == 64 || dm.B == 128);
+}
+
 void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {
   const size_t nb = (size_t)dm.nb;
   size_t off = 0;
@@ -95,7 +102,8 @@ void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {
   w->indices = off;
   off = align_up(off + (size_t)dm.Hq * (nb * (nb + 1) / 2) * sizeof(int));
   w->v_t = off;
-  if (use_mfma(p, dm)) off = align_up(off + (size_t)dm.Hkv * dm.d * nb * dm.B * sizeof(uint16_t));
+  if (use_mfma(p, dm) || use_small(p, dm))
+    off = align_up(off + (size_t)dm.Hkv * dm.d * nb * dm.B * sizeof(uint16_t));
   w->total = off;
 }
 
@@ -362,6 +370,10 @@ int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_byt
     uint16_t* v_t = at<uint16_t>(workspace, w.v_t);
     e = fpk_launch_vtrans(*p, dm, v_t, st);
     if (e == hipSuccess) e = fpk_launch_attn_mfma(*p, dm, counts, indices, v_t, sc, st);
+  } else if (use_small(p, dm)) {
+    uint16_t* v_t = at<uint16_t>(workspace, w.v_t);
+    e = fpk_launch_vtrans(*p, dm, v_t, st);
+    if (e == hipSuccess) e = fpk_launch_attn_small(*p, dm, counts, indices, v_t, sc, st);
   } else {
     e = fpk_launch_attn_generic(*p, dm, counts, indices, sc, st);
   }

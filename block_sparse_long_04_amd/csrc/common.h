@@ -89,5 +89,9 @@ hipError_t fpk_launch_attn_mfma(const fp_problem& p, const FpDims& dm, const int
 hipError_t fpk_launch_attn_pack(const fp_problem& p, const FpDims& dm, const int* counts, const int* indices,
                                 const uint16_t* v_t, float sm_scale, hipStream_t st);
 
+// bf16 layers with head_dim or block_size 64 on the matrix cores.
+hipError_t fpk_launch_attn_small(const fp_problem& p, const FpDims& dm, const int* counts, const int* indices,
+                                 const uint16_t* v_t, float sm_scale, hipStream_t st);
+
 hipError_t fpk_launch_attn_generic(const fp_problem& p, const FpDims& dm, const int* counts,
                                    const int* indices, float sm_scale, hipStream_t st);

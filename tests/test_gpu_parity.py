@@ -90,6 +90,23 @@ def test_dense_tau_zero_matches_textbook_attention():
     check_out(res["out"], dense, "bf16")
 
 
+@pytest.mark.parametrize("d,B,L", [(64, 64, 64 * 150 + 17), (64, 128, 128 * 70 + 5), (128, 64, 64 * 130 + 33)])
+def test_dense_lists_past_one_window(d, B, L):
+    # tau = 0 keeps every causal block: the late query blocks' lists run past
+    # 64 and 128 entries, the size of the list window the d / B = 64 kernel
+    # reads with one load.
+    dev = require_gpu()
+    cfg = CONFIGS["c2"].with_(seq_len=L, num_q_heads=2, num_kv_heads=1, head_dim=d, block_size=B)
+    say(f"[dense long lists] d={d} B={B} L={L}")
+    layer = make_layer(cfg)
+    _, res = run_gpu(layer, 0.0, dev)
+    nb = cfg.num_blocks
+    assert all(len(res["lists"][h][i]) == i + 1 for h in range(2) for i in range(nb))
+    q, k, v = (t.numpy() for t in (layer.q32, layer.k32, layer.v32))
+    dense = O.dense_causal_attention(q, k, v, sm_scale(layer))
+    check_out(res["out"], dense, "bf16")
+
+
 @pytest.mark.parametrize("L", [1, 77, 128, 129, 256])
 def test_degenerate_lengths(L):
     dev = require_gpu()
