@@ -44,6 +44,26 @@ __device__ __forceinline__ int slot_of(int r, int c) {
   return kRowBytes == 128 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
 }
 
+// Maximum of the NKT sub-tiles' 16 values per lane, with v_max3_f32 written
+// out: fmaxf would first canonicalise each operand (one more instruction per
+// value), which scores fresh from the matrix cores do not need.
+template <int NKT>
+__device__ __forceinline__ float block_max(const floatx16* s) {
+  float acc[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    acc[kt] = max3_late(s[kt][0], s[kt][1], s[kt][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) acc[kt] = max3_late(acc[kt], s[kt][r], s[kt][r + 1]);
+    acc[kt] = max3_late(acc[kt], s[kt][15], s[kt][15]);
+  }
+  float m = acc[0];
+#pragma unroll
+  for (int kt = 1; kt < NKT; kt += 2)
+    m = kt + 1 < NKT ? max3_late(m, acc[kt], acc[kt + 1]) : max3_late(m, acc[kt], acc[kt]);
+  return m;
+}
+
 // Issues one key block's K and V^T tiles into ring stage stg: LPW 1 KiB
 // buffer_load ... lds per tile for this wave (its chunks of the tile).
 template <int D, int BS>
@@ -54,12 +74,11 @@ struct SmallLoader {
   const uint8_t* kg;   // K of this kv head
   const uint16_t* vg;  // V^T of this kv head
   int k_row, L, v_bytes;
-  uint4* sK;  // this wave's part of ring stage 0 (K)
-  uint4* sV;  // (V^T)
+  int wave_off;  // this wave's first chunk of a tile
   uint32_t koff[LPW], voff[LPW];
   int krow[LPW];
 
-  __device__ __forceinline__ void load(int j, int stg) const {
+  __device__ __forceinline__ void load(int j, uint4* dk, uint4* dv) const {
     const int present = min(BS, L - j * BS);
     const int ext = (j >= 0 && present > 0) ? (present - 1) * k_row + KRB : 0;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -71,17 +90,17 @@ struct SmallLoader {
       uint32_t ko = koff[e];
       if (krow[e] >= present)  // ragged last block: repeat row L - 1
         ko = (uint32_t)((present - 1) * k_row) + (koff[e] - (uint32_t)(krow[e] * k_row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sK + stg * TCH + 64 * e), 16, ko, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(dk + wave_off + 64 * e), 16, ko, 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < LPW; ++e)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(sV + stg * TCH + 64 * e), 16, voff[e],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dv + wave_off + 64 * e), 16, voff[e],
                                                j * BS * 2, 0, 0);
   }
 };
 
-template <int D, int BS>
-__global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
+template <int D, int BS, int kWaves>
+__global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))) void attn_small_kernel(SmallArgs a) {
   constexpr int NKT = BS / 32;       // 32-key sub-tiles per block
   constexpr int KST = D / 16;        // head-dim steps of S^T
   constexpr int NDT = D / 32;        // head-dim tiles of O^T
@@ -91,10 +110,8 @@ __global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
   constexpr int TCH = BS * D / 8;    // 16-byte chunks of a K tile (= of a V^T tile)
   constexpr int NW = BS / 32;        // waves
   constexpr int LPW = TCH / (64 * NW);  // 1 KiB loads per wave per tile
-  constexpr int NS = 3;              // ring stages
   static_assert(TCH % (64 * NW) == 0, "tile loads split evenly over the waves");
-  __shared__ uint4 sK[NS][TCH];
-  __shared__ uint4 sV[NS][TCH];
+  __shared__ uint4 smem[4 * TCH];  // K stage 0, K stage 1, V^T stage 0, V^T stage 1
 
   const int h = blockIdx.x % a.Hq;
   const int i = a.nb - 1 - (int)(blockIdx.x / a.Hq);  // late (heavy) query blocks first
@@ -148,8 +165,7 @@ __global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
   ld.k_row = (int)(a.k_st * 2);
   ld.L = a.L;
   ld.v_bytes = D * a.Lpad * 2;
-  ld.sK = &sK[0][0] + 64 * LPW * w;
-  ld.sV = &sV[0][0] + 64 * LPW * w;
+  ld.wave_off = 64 * LPW * w;
 #pragma unroll
   for (int e = 0; e < LPW; ++e) {
     const int ch = 64 * (LPW * w + e) + lane;
@@ -159,39 +175,14 @@ __global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
     const int vr = ch / (VRB / 16), vs = ch % (VRB / 16);
     ld.voff[e] = (uint32_t)(vr * a.Lpad * 2 + slot_of<VRB>(vr, vs) * 16);
   }
-  auto load_block = [&](int j, int stg) { ld.load(j, stg); };
 
   floatx16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = (floatx16){0};
   float m_run = -INFINITY, l = 0.f;
 
-  // prologue: blocks 0 and 1 in flight (entry() is called once per list
-  // position, in order: its window only moves forward)
-  int j_cur = entry(0);
-  int j_nxt = cnt > 1 ? entry(1) : -1;
-  load_block(j_cur, 0);
-  if (cnt > 1) load_block(j_nxt, 1);
-  int stg = 0;
-  for (int n = 0; n < cnt; ++n) {
-    const int j = j_cur;
-    // block n has landed (block n + 1 may still be in flight); after the
-    // barrier every wave is done with block n - 1, whose stage takes n + 2
-    constexpr int kYoung = 2 * LPW;  // one block's loads of this wave
-    static_assert(kYoung < 64, "vmcnt range");
-    if (n + 1 < cnt) __builtin_amdgcn_s_waitcnt(0x0070 | (kYoung & 15) | ((kYoung >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (n + 2 < cnt) {
-      const int j2 = entry(n + 2);
-      load_block(j2, stg == 0 ? 2 : stg - 1);
-      j_cur = j_nxt;
-      j_nxt = j2;
-    } else {
-      j_cur = j_nxt;
-    }
+  // One key block j from the tiles sKc (K) and sVc (V^T).
+  auto block_step = [&](int j, const uint4* sKc, const uint4* sVc) {
     // S^T = K Q^T, sub-tile by sub-tile
     floatx16 s[NKT];
 #pragma unroll
@@ -201,17 +192,14 @@ __global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
 #pragma unroll
       for (int st = 0; st < KST; ++st)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(&sK[stg][r * (KRB / 16) + slot_of<KRB>(r, 2 * st + hh)]), qf[st],
+            *reinterpret_cast<const bf16x8*>(&sKc[r * (KRB / 16) + slot_of<KRB>(r, 2 * st + hh)]), qf[st],
             s[kt], 0, 0, 0);
     }
     if (j == i) {  // causal mask of the diagonal block
 #pragma unroll
       for (int kh = 0; kh < NKT / 2; ++kh) mask_diag(s + 2 * kh, w, kh, qi, hh);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < NKT; kt += 2) mx = fmaxf(mx, tile_max(s + kt));
-    mx = pair_max(mx);
+    const float mx = pair_max(block_max<NKT>(s));
     const float mxs = mx * c;
     if (__any(mxs > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mxs);
@@ -238,10 +226,44 @@ __global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
       for (int dt = 0; dt < NDT; ++dt) {
         const int r = 32 * dt + qi;
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(&sV[stg][r * (VRB / 16) + slot_of<VRB>(r, 2 * u + hh)]),
+            *reinterpret_cast<const bf16x8*>(&sVc[r * (VRB / 16) + slot_of<VRB>(r, 2 * u + hh)]),
             as_bf16x8(pw[u]), o[dt], 0, 0, 0);
       }
-    stg = stg == 2 ? 0 : stg + 1;
+  };
+
+  // Two stages; two list positions per trip so each stage's role is static
+  // (the loads into one stage and the reads of the other then carry
+  // distinct addresses the compiler can tell apart, and no wait for the
+  // loads in flight is placed before the reads).  entry() is called once
+  // per list position, in order: its window only moves forward.
+  uint4* const sK0 = smem;
+  uint4* const sK1 = smem + TCH;
+  uint4* const sV0 = smem + 2 * TCH;
+  uint4* const sV1 = smem + 3 * TCH;
+  int j_cur = entry(0);
+  ld.load(j_cur, sK0, sV0);
+  for (int n = 0; n < cnt; n += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int t = n + half;
+      if (half == 1 && t >= cnt) break;
+      const uint4* sKc = half == 0 ? sK0 : sK1;
+      const uint4* sVc = half == 0 ? sV0 : sV1;
+      uint4* sKn = half == 0 ? sK1 : sK0;
+      uint4* sVn = half == 0 ? sV1 : sV0;
+      const int j = j_cur;
+      // block t has landed; after the barrier every wave is done with block
+      // t - 1, whose stage takes block t + 1
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 1 < cnt) {
+        j_cur = entry(t + 1);
+        ld.load(j_cur, sKn, sVn);
+      }
+      block_step(j, sKc, sVc);
+    }
   }
 
   // Normalise and write out: lane holds dims 32 dt + 8 q4 + 4 hh + 0..3 of token qi.
@@ -262,9 +284,12 @@ __global__ __launch_bounds__(BS * 2) void attn_small_kernel(SmallArgs a) {
   }
 }
 
-template __global__ void attn_small_kernel<64, 64>(SmallArgs);
-template __global__ void attn_small_kernel<64, 128>(SmallArgs);
-template __global__ void attn_small_kernel<128, 64>(SmallArgs);
+// The waves per SIMD each variant's registers are sized for (LDS: two
+// stages of K and V^T, 4 B D 2 bytes per workgroup, of 160 KiB per CU).
+constexpr int kWv6464 = 3, kWv64128 = 2, kWv12864 = 1;
+template __global__ void attn_small_kernel<64, 64, kWv6464>(SmallArgs);
+template __global__ void attn_small_kernel<64, 128, kWv64128>(SmallArgs);
+template __global__ void attn_small_kernel<128, 64, kWv12864>(SmallArgs);
 
 }  // namespace
 
@@ -291,10 +316,10 @@ hipError_t fpk_launch_attn_small(const fp_problem& p, const FpDims& dm, const in
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(dm.nb * dm.Hq));
   if (dm.d == 64 && dm.B == 64)
-    hipLaunchKernelGGL((attn_small_kernel<64, 64>), grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((attn_small_kernel<64, 64, kWv6464>), grid, dim3(128), 0, st, a);
   else if (dm.d == 64)
-    hipLaunchKernelGGL((attn_small_kernel<64, 128>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_small_kernel<64, 128, kWv64128>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_small_kernel<128, 64>), grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((attn_small_kernel<128, 64, kWv12864>), grid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
