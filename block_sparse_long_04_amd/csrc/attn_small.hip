@@ -6,21 +6,23 @@
 // the identified blocks); GQA per the FlashPrefill V2 abstract.
 //
 // One workgroup = one (q head h, query block i): B / 32 waves, wave w owning
-// query rows 32w .. 32w+31.  Per listed key block:
-//   * the K tile [B keys][D dims] and the V^T tile [D dims][B keys] (V^T
+// query rows 32w .. 32w+31.  The listed key blocks are walked in units of 64
+// keys (B / 64 units per block).  Per unit:
+//   * the K tile [64 keys][D dims] and the V^T tile [D dims][64 keys] (V^T
 //     written by this call's layout pass) travel global -> LDS with
-//     buffer_load ... lds into a ring of three stages: block n + 2 is
-//     requested while block n is computed, one barrier per block;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, one 32-key sub-tile at a
-//     time, D / 16 steps; K rows are fed in the order pm(m) (bits 2 and 3
-//     swapped) so each lane holds runs of 8 consecutive keys, the B operand
-//     of P.V as is (the same conventions as attn_mfma.hip);
+//     buffer_load ... lds into a ring of NS stages: unit t + NS - 1 is
+//     requested while unit t is computed, one barrier per unit;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, two 32-key sub-tiles, D / 16
+//     steps each; K rows are fed in the order pm(m) (bits 2 and 3 swapped) so
+//     each lane holds runs of 8 consecutive keys, the B operand of P.V as is
+//     (the same conventions as attn_mfma.hip);
 //   * online softmax in the exp2 domain with the lazy maximum of
 //     attn_mfma.hip; the causal mask on the diagonal block only;
-//   * O^T += V^T P^T, D / 32 head-dim tiles by B / 16 key groups.
-// LDS rows of 128 B (K with D = 64, V^T with B = 64) hold their eight 16-byte
-// chunks at chunk ^ ((row >> 1) & 7), rows of 256 B at chunk ^ (row & 15):
-// the 16 rows a 16-byte operand read touches land on distinct bank slots.
+//   * O^T += V^T P^T, D / 32 head-dim tiles by 4 key groups of 16.
+// LDS rows of 128 B (K with D = 64, every V^T unit row) hold their eight
+// 16-byte chunks at chunk ^ ((row >> 1) & 7), rows of 256 B (K with D = 128)
+// at chunk ^ (row & 15): the 16 rows a 16-byte operand read touches land on
+// distinct bank slots.
 #include "attn_common.h"
 
 namespace {
@@ -64,12 +66,16 @@ __device__ __forceinline__ float block_max(const floatx16* s) {
   return m;
 }
 
-// Issues one key block's K and V^T tiles into ring stage stg: LPW 1 KiB
-// buffer_load ... lds per tile for this wave (its chunks of the tile).
+// Issues one 64-key unit's K and V^T tiles (key block j, keys 64 hf ..
+// 64 hf + 63 of it) into the stage at dk / dv: LPW 1 KiB buffer_load ... lds
+// per tile for this wave (its chunks of the tile).  K rows come through a
+// buffer resource per unit (extent up to the unit's last present row; rows
+// past L repeat row L - 1 and a unit wholly past L reads zeros, masked
+// later), V^T rows through one resource per kv head (zero past L).
 template <int D, int BS>
-struct SmallLoader {
+struct UnitLoader {
   static constexpr int KRB = D * 2;
-  static constexpr int TCH = BS * D / 8;
+  static constexpr int TCH = 64 * D / 8;
   static constexpr int LPW = TCH / (64 * (BS / 32));
   const uint8_t* kg;   // K of this kv head
   const uint16_t* vg;  // V^T of this kv head
@@ -78,43 +84,43 @@ struct SmallLoader {
   uint32_t koff[LPW], voff[LPW];
   int krow[LPW];
 
-  __device__ __forceinline__ void load(int j, uint4* dk, uint4* dv) const {
-    const int present = min(BS, L - j * BS);
-    const int ext = (j >= 0 && present > 0) ? (present - 1) * k_row + KRB : 0;
+  __device__ __forceinline__ void load(int j, int hf, uint4* dk, uint4* dv) const {
+    const int key0 = j * BS + 64 * hf;
+    const int present = min(64, L - key0);
+    const int ext = present > 0 ? (present - 1) * k_row + KRB : 0;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(kg + (int64_t)j * BS * k_row), 0, ext, 0x00020000);
+        const_cast<uint8_t*>(kg + (int64_t)key0 * k_row), 0, ext, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg), 0, v_bytes, 0x00020000);
 #pragma unroll
     for (int e = 0; e < LPW; ++e) {
       uint32_t ko = koff[e];
-      if (krow[e] >= present)  // ragged last block: repeat row L - 1
+      if (krow[e] >= present)  // ragged last unit: repeat row L - 1
         ko = (uint32_t)((present - 1) * k_row) + (koff[e] - (uint32_t)(krow[e] * k_row));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(dk + wave_off + 64 * e), 16, ko, 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < LPW; ++e)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dv + wave_off + 64 * e), 16, voff[e],
-                                               j * BS * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dv + wave_off + 64 * e), 16, voff[e], key0 * 2,
+                                               0, 0);
   }
 };
 
-template <int D, int BS, int kWaves>
+template <int D, int BS, int NS, int kWaves>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))) void attn_small_kernel(SmallArgs a) {
-  constexpr int NKT = BS / 32;       // 32-key sub-tiles per block
+  constexpr int UPB = BS / 64;       // 64-key units per key block
   constexpr int KST = D / 16;        // head-dim steps of S^T
   constexpr int NDT = D / 32;        // head-dim tiles of O^T
-  constexpr int NU = BS / 16;        // 16-key groups of P.V
   constexpr int KRB = D * 2;         // K row bytes in LDS
-  constexpr int VRB = BS * 2;        // V^T row bytes in LDS
-  constexpr int TCH = BS * D / 8;    // 16-byte chunks of a K tile (= of a V^T tile)
+  constexpr int TCH = 64 * D / 8;    // 16-byte chunks of a K unit tile (= of a V^T unit tile)
   constexpr int NW = BS / 32;        // waves
   constexpr int LPW = TCH / (64 * NW);  // 1 KiB loads per wave per tile
+  static_assert(NS == 2 || NS == 3, "ring stages");
   static_assert(TCH % (64 * NW) == 0, "tile loads split evenly over the waves");
-  __shared__ uint4 smem[4 * TCH];  // K stage 0, K stage 1, V^T stage 0, V^T stage 1
+  __shared__ uint4 smem[2 * NS * TCH];  // K stages 0 .. NS-1, then V^T stages 0 .. NS-1
 
-  const int h = blockIdx.x % a.Hq;
-  const int i = a.nb - 1 - (int)(blockIdx.x / a.Hq);  // late (heavy) query blocks first
+  int h, i;  // XCD-aware order: the workgroups an XCD runs together share a kv group
+  work_item(blockIdx.x, a.nb, a.Hq, a.Hkv, h, i);
   const int g = h / (a.Hq / a.Hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,14 +158,11 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
       qf[s] = *reinterpret_cast<const bf16x8*>(a.q + (int64_t)tq * a.q_st + (int64_t)h * a.q_sh + 16 * s + 8 * hh);
   }
 
-  // Direct-to-LDS tile loads.  Load e of wave w moves 1 KiB: lane l writes
-  // 16-byte chunk (64 (LPW w + e) + l) of the tile, i.e. row r = that / (row
-  // chunks), slot = that % (row chunks), fetching the row's global chunk
-  // slot_of(r, .) maps there (an involution).  K rows come through a buffer
-  // resource per key block (extent up to the block's last present row; rows
-  // past L repeat row L - 1, masked later), V^T rows through one resource
-  // per kv head (zero past L).
-  SmallLoader<D, BS> ld;
+  // Load e of wave w moves 1 KiB: lane l writes 16-byte chunk
+  // (64 (LPW w + e) + l) of the tile, i.e. row r = that / (row chunks),
+  // slot = that % (row chunks), fetching the row's global chunk slot_of(r, .)
+  // maps there (an involution).
+  UnitLoader<D, BS> ld;
   ld.kg = reinterpret_cast<const uint8_t*>(a.k + (int64_t)g * a.k_sh);
   ld.vg = a.vt + (int64_t)g * D * a.Lpad;
   ld.k_row = (int)(a.k_st * 2);
@@ -172,8 +175,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
     const int kr = ch / (KRB / 16), ks = ch % (KRB / 16);
     ld.krow[e] = kr;
     ld.koff[e] = (uint32_t)(kr * ld.k_row + slot_of<KRB>(kr, ks) * 16);
-    const int vr = ch / (VRB / 16), vs = ch % (VRB / 16);
-    ld.voff[e] = (uint32_t)(vr * a.Lpad * 2 + slot_of<VRB>(vr, vs) * 16);
+    const int vr = ch / 8, vs = ch % 8;
+    ld.voff[e] = (uint32_t)(vr * a.Lpad * 2 + slot_of<128>(vr, vs) * 16);
   }
 
   floatx16 o[NDT];
@@ -181,12 +184,13 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
   for (int dt = 0; dt < NDT; ++dt) o[dt] = (floatx16){0};
   float m_run = -INFINITY, l = 0.f;
 
-  // One key block j from the tiles sKc (K) and sVc (V^T).
-  auto block_step = [&](int j, const uint4* sKc, const uint4* sVc) {
-    // S^T = K Q^T, sub-tile by sub-tile
-    floatx16 s[NKT];
+  // One unit: keys 64 hf .. 64 hf + 63 of key block j, from the tiles sKc
+  // (K) and sVc (V^T).
+  auto unit_step = [&](int j, int hf, const uint4* sKc, const uint4* sVc) {
+    // S^T = K Q^T, two 32-key sub-tiles
+    floatx16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
       const int r = 32 * kt + pm;
       s[kt] = (floatx16){0};
 #pragma unroll
@@ -195,11 +199,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
             *reinterpret_cast<const bf16x8*>(&sKc[r * (KRB / 16) + slot_of<KRB>(r, 2 * st + hh)]), qf[st],
             s[kt], 0, 0, 0);
     }
-    if (j == i) {  // causal mask of the diagonal block
-#pragma unroll
-      for (int kh = 0; kh < NKT / 2; ++kh) mask_diag(s + 2 * kh, w, kh, qi, hh);
-    }
-    const float mx = pair_max(block_max<NKT>(s));
+    if (j == i) mask_diag(s, w, hf, qi, hh);  // causal mask of the diagonal block
+    const float mx = pair_max(block_max<2>(s));
     const float mxs = mx * c;
     if (__any(mxs > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mxs);
@@ -211,9 +212,9 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
     }
     const float mu = m_run == -INFINITY ? 0.0f : m_run;
     // P in bf16 pairs: group u = keys 16 u .. 16 u + 15 (sub-tile u / 2, registers 8 (u % 2) ..)
-    uint32_t pw[NU][4];
+    uint32_t pw[4][4];
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * (u & 1) + 2 * e;
@@ -221,48 +222,55 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
       }
     // O^T += V^T P^T
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int r = 32 * dt + qi;
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(&sVc[r * (VRB / 16) + slot_of<VRB>(r, 2 * u + hh)]),
-            as_bf16x8(pw[u]), o[dt], 0, 0, 0);
+            *reinterpret_cast<const bf16x8*>(&sVc[r * 8 + slot_of<128>(r, 2 * u + hh)]), as_bf16x8(pw[u]),
+            o[dt], 0, 0, 0);
       }
   };
 
-  // Two stages; two list positions per trip so each stage's role is static
-  // (the loads into one stage and the reads of the other then carry
-  // distinct addresses the compiler can tell apart, and no wait for the
-  // loads in flight is placed before the reads).  entry() is called once
-  // per list position, in order: its window only moves forward.
-  uint4* const sK0 = smem;
-  uint4* const sK1 = smem + TCH;
-  uint4* const sV0 = smem + 2 * TCH;
-  uint4* const sV1 = smem + 3 * TCH;
-  int j_cur = entry(0);
-  ld.load(j_cur, sK0, sV0);
-  for (int n = 0; n < cnt; n += 2) {
+  // NS stages; NS units per trip so each stage's role is static (the loads
+  // into one stage and the reads of another then carry addresses the
+  // compiler can tell apart, and no wait for the loads in flight is placed
+  // before the reads).  entry() is called once per list position, in order:
+  // its window only moves forward.
+  const int U = cnt * UPB;
+  int jst[NS];     // key block of the unit each stage holds
+  int j_last = 0;  // key block of the last unit issued
+  auto issue = [&](int t, int p) {
+    const int hf = UPB == 1 ? 0 : t % UPB;
+    if (hf == 0) j_last = entry(t / UPB);
+    jst[p] = j_last;
+    ld.load(j_last, hf, smem + p * TCH, smem + (NS + p) * TCH);
+  };
+  // Q and the first list window have landed before the first unit's loads
+  // are issued: otherwise the first uses of their registers, inside the
+  // loop, would wait for every load in flight on each trip.
+  FP_WAIT_VMEM();
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int t = n + half;
-      if (half == 1 && t >= cnt) break;
-      const uint4* sKc = half == 0 ? sK0 : sK1;
-      const uint4* sVc = half == 0 ? sV0 : sV1;
-      uint4* sKn = half == 0 ? sK1 : sK0;
-      uint4* sVn = half == 0 ? sV1 : sV0;
-      const int j = j_cur;
-      // block t has landed; after the barrier every wave is done with block
-      // t - 1, whose stage takes block t + 1
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  for (int p = 0; p + 1 < NS; ++p)
+    if (p < U) issue(p, p);
+  for (int t0 = 0; t0 < U; t0 += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      const int t = t0 + p;
+      if (p > 0 && t >= U) break;
+      // unit t has landed (with three stages unit t + 1 may still be in
+      // flight); after the barrier every wave is done with unit t - 1, whose
+      // stage takes unit t + NS - 1
+      constexpr int kYoung = 2 * LPW;  // one unit's loads of this wave
+      static_assert(kYoung < 64, "vmcnt range");
+      if (NS == 3 && t + 1 < U) __builtin_amdgcn_s_waitcnt(0x0070 | (kYoung & 15) | ((kYoung >> 4) << 14));
+      else __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (t + 1 < cnt) {
-        j_cur = entry(t + 1);
-        ld.load(j_cur, sKn, sVn);
-      }
-      block_step(j, sKc, sVc);
+      const int j = jst[p];
+      if (t + NS - 1 < U) issue(t + NS - 1, (p + NS - 1) % NS);
+      unit_step(j, UPB == 1 ? 0 : t % UPB, smem + p * TCH, smem + (NS + p) * TCH);
     }
   }
 
@@ -284,12 +292,14 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(kWaves))
   }
 }
 
-// The waves per SIMD each variant's registers are sized for (LDS: two
-// stages of K and V^T, 4 B D 2 bytes per workgroup, of 160 KiB per CU).
-constexpr int kWv6464 = 3, kWv64128 = 2, kWv12864 = 1;
-template __global__ void attn_small_kernel<64, 64, kWv6464>(SmallArgs);
-template __global__ void attn_small_kernel<64, 128, kWv64128>(SmallArgs);
-template __global__ void attn_small_kernel<128, 64, kWv12864>(SmallArgs);
+// Ring stages and the waves per SIMD the registers are sized for, per
+// variant (LDS: 2 NS 64 D 2 bytes per workgroup, of 160 KiB per CU).
+constexpr int kNs6464 = 2, kWv6464 = 3;
+constexpr int kNs64128 = 3, kWv64128 = 3;
+constexpr int kNs12864 = 2, kWv12864 = 1;
+template __global__ void attn_small_kernel<64, 64, kNs6464, kWv6464>(SmallArgs);
+template __global__ void attn_small_kernel<64, 128, kNs64128, kWv64128>(SmallArgs);
+template __global__ void attn_small_kernel<128, 64, kNs12864, kWv12864>(SmallArgs);
 
 }  // namespace
 
@@ -316,10 +326,10 @@ hipError_t fpk_launch_attn_small(const fp_problem& p, const FpDims& dm, const in
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(dm.nb * dm.Hq));
   if (dm.d == 64 && dm.B == 64)
-    hipLaunchKernelGGL((attn_small_kernel<64, 64, kWv6464>), grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((attn_small_kernel<64, 64, kNs6464, kWv6464>), grid, dim3(128), 0, st, a);
   else if (dm.d == 64)
-    hipLaunchKernelGGL((attn_small_kernel<64, 128, kWv64128>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_small_kernel<64, 128, kNs64128, kWv64128>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_small_kernel<128, 64, kWv12864>), grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((attn_small_kernel<128, 64, kNs12864, kWv12864>), grid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
