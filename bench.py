@@ -118,10 +118,26 @@ ATTN_SOURCES = {
     "pack": ["block_sparse_long_04_amd/csrc/attn_pack.hip",
              "block_sparse_long_04_amd/csrc/attn_common.h",
              "block_sparse_long_04_amd/csrc/common.h"],
+    "small": ["block_sparse_long_04_amd/csrc/attn_small.hip",
+              "block_sparse_long_04_amd/csrc/attn_common.h",
+              "block_sparse_long_04_amd/csrc/common.h"],
+    "generic": ["block_sparse_long_04_amd/csrc/attn_generic.hip",
+                "block_sparse_long_04_amd/csrc/common.h"],
 }
 
 
-def measured_traffic(workload: str, attention: str = "default"):
+def attention_kernel(dtype: str, d: int, B: int, attention: str = "default") -> str:
+    """Which attention kernel a layer runs: the d = B = 128 matrix-core kernel
+    (bf16 / e4m3; its two-heads variant when asked), the 64-key-unit
+    matrix-core kernel for bf16 with d or B = 64, else the generic one."""
+    if dtype in ("bf16", "fp8") and d == 128 and B == 128:
+        return "pack" if attention == "pack" else "default"
+    if dtype == "bf16" and d in (64, 128) and B in (64, 128):
+        return "small"
+    return "generic"
+
+
+def measured_traffic(workload: str, kernel: str = "default"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary, only if it was taken on the current attention source."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
@@ -131,7 +147,7 @@ def measured_traffic(workload: str, attention: str = "default"):
         rec = json.load(open(path)).get(workload)
     except Exception:
         return None
-    if not rec or rec.get("source_hash") != source_hash(ATTN_SOURCES[attention]):
+    if not rec or rec.get("source_hash") != source_hash(ATTN_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -459,19 +475,19 @@ def main():
     flops = 4.0 * d * pairs
     density = float(counts.sum()) / (Hq * nb * (nb + 1) / 2)
     esz = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.dtype]
-    # matrix cores: bf16 / e4m3 with d = B = 128, or bf16 with d, B in {64, 128}
-    mfma_path = (cfg.dtype in ("bf16", "fp8") and d == 128 and B == 128) or cfg.dtype == "bf16"
+    kernel = attention_kernel(cfg.dtype, d, B, args.attention)
+    mfma_path = kernel != "generic"  # matrix cores (and the V^T layout pass in the stage)
     # algorithmic bytes of step 1: Q and K read once, the pooled proxies written
     pool_bytes = L * (Hq + Hkv) * d * esz + (Hq + Hkv) * nb * d * 4
     sel_flops = 2.0 * d * Hq * nb * (nb + 1) / 2
     attn_tflops = flops / (stage_ms["attention"] * 1e-3) / 1e12
-    # matrix-core attention for bf16 / e4m3 with d = B = 128; otherwise the
-    # generic kernel, fp32 vector ALUs
+    # matrix-core attention (bf16 / e4m3); the generic kernel (fp32 inputs)
+    # runs on the fp32 vector ALUs
     bound = "mfma" if mfma_path else "alu"
     peak = PEAK["fp8"] if cfg.dtype == "fp8" else (PEAK["bf16"] if mfma_path else PEAK["fp32"])
     wl = (cfg.name + f"_tau{tau:g}" + ("_group" if args.select == "group" else "")
           + ("_pack" if args.attention == "pack" else ""))
-    traffic = measured_traffic(wl, args.attention)
+    traffic = measured_traffic(wl, kernel)
     res = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -508,6 +524,7 @@ def main():
         "roofline": {"bound": bound, "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": traffic},
+        "attention_kernel": kernel,
         "attention_stage_includes_vt_pass": bool(mfma_path),
         "cpu_baseline": None,
     }

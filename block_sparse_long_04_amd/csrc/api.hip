@@ -81,11 +81,14 @@ bool use_mfma(const fp_problem* p, const FpDims& dm) {
   return (int64_t)dm.B * p->k_stride_tok * esz + dm.d * esz < (int64_t(1) << 31);
 }
 
-// bf16 layers with head_dim or block_size 64 (d, B in {64, 128}) take the
-// matrix-core kernel of attn_small.hip (d = B = 128 takes attn_mfma.hip).
+// bf16 layers with head_dim or block_size 64 (d, B in {64, 128}, not both
+// 128: that shape takes attn_mfma.hip) take the matrix-core kernel of
+// attn_small.hip.  Its K buffer resources span one 64-key unit, so the same
+// 31-bit extent limit applies to 64 rows.
 bool use_small(const fp_problem* p, const FpDims& dm) {
-  if (p->dtype != FP_BF16 || use_mfma(p, dm)) return false;
-  return (dm.d == 64 || dm.d == 128) && (dm.B == 64 || dm.B == 128);
+  if (p->dtype != FP_BF16 || (dm.d == 128 && dm.B == 128)) return false;
+  if (!((dm.d == 64 || dm.d == 128) && (dm.B == 64 || dm.B == 128))) return false;
+  return (int64_t)64 * p->k_stride_tok * 2 + dm.d * 2 < (int64_t(1) << 31);
 }
 
 void layout_of(const fp_problem* p, const FpDims& dm, fp_ws_layout* w) {

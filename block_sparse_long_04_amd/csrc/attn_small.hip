@@ -327,9 +327,11 @@ hipError_t fpk_launch_attn_small(const fp_problem& p, const FpDims& dm, const in
   const dim3 grid((unsigned)(dm.nb * dm.Hq));
   if (dm.d == 64 && dm.B == 64)
     hipLaunchKernelGGL((attn_small_kernel<64, 64, kNs6464, kWv6464>), grid, dim3(128), 0, st, a);
-  else if (dm.d == 64)
+  else if (dm.d == 64 && dm.B == 128)
     hipLaunchKernelGGL((attn_small_kernel<64, 128, kNs64128, kWv64128>), grid, dim3(256), 0, st, a);
-  else
+  else if (dm.d == 128 && dm.B == 64)
     hipLaunchKernelGGL((attn_small_kernel<128, 64, kNs12864, kWv12864>), grid, dim3(128), 0, st, a);
+  else
+    return hipErrorInvalidValue;  // no variant for this shape
   return hipGetLastError();
 }

@@ -69,3 +69,18 @@ def test_traffic_record_needs_the_current_attention_source(tmp_path, monkeypatch
         f.write(b"\n")
     assert bench.measured_traffic("w_pack", "pack") is None
     assert bench.measured_traffic("w") == 123
+
+
+def test_attention_kernel_follows_the_library_dispatch():
+    # the same rule as the library's dispatch: d = B = 128 bf16 / e4m3 on the
+    # 128-wide kernel, other bf16 shapes with d, B in {64, 128} on the 64-key
+    # unit kernel, the rest (fp32, e4m3 with d or B = 64) on the generic one
+    assert bench.attention_kernel("bf16", 128, 128) == "default"
+    assert bench.attention_kernel("fp8", 128, 128) == "default"
+    assert bench.attention_kernel("bf16", 128, 128, "pack") == "pack"
+    assert bench.attention_kernel("bf16", 64, 64) == "small"
+    assert bench.attention_kernel("bf16", 64, 128) == "small"
+    assert bench.attention_kernel("bf16", 128, 64) == "small"
+    assert bench.attention_kernel("fp8", 64, 128) == "generic"
+    assert bench.attention_kernel("f32", 128, 128) == "generic"
+    assert bench.attention_kernel("f32", 64, 64) == "generic"
