@@ -100,7 +100,8 @@ typedef struct fp_problem {
  *   v_t     bf16 [num_kv_heads][head_dim][nb*block_size]  scratch of fp_sparse_prefill: V
  *           transposed per kv head (the key-contiguous rows its P.V products read), zero past
  *           seq_len; e4m3 codes widened to bf16 exactly, v_scale applied at the output
- *           (zero-length unless the input is bf16 or e4m3 with head_dim 128 and block_size 128)
+ *           (zero-length unless the attention runs on the matrix cores: bf16 or e4m3 with
+ *           head_dim 128 and block_size 128, or bf16 with head_dim and block_size in {64, 128})
  * The layout is part of the ABI: a caller may read the selection, or write
  * its own counts/indices (ascending, each list ending with its diagonal
  * block i) before fp_sparse_prefill to run attention on a given mask. */
@@ -161,9 +162,11 @@ int fp_block_select_sorted(const fp_problem* p, int rule, float param, void* wor
  * (FP_ERR_UNSUPPORTED otherwise). */
 int fp_block_select_probe(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Step 5.  Reads q, k, v, counts and indices; writes out (and, for bf16 or
- * e4m3 inputs with head_dim 128 and block_size 128, first the v_t section,
- * from v, which its attention kernel then reads). */
+/* Step 5.  Reads q, k, v, counts and indices; writes out.  On the matrix
+ * cores (bf16 or e4m3 with head_dim 128 and block_size 128; bf16 with
+ * head_dim and block_size in {64, 128}) it first writes the v_t section from
+ * v, which its attention kernel then reads; other layers (fp32 inputs, e4m3
+ * with head_dim or block_size 64) run on the vector ALUs. */
 int fp_sparse_prefill(const fp_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 5 with the two query heads of a pair (2p, 2p+1) of one kv group served
