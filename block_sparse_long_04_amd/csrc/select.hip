@@ -59,19 +59,48 @@ __host__ __device__ __forceinline__ int groups_of(int ntiles, int S) {
 // words so pass 3 reads a word with one 8-byte load.
 __host__ __device__ __forceinline__ int mask_stride(int ntiles) { return (ntiles + 3) & ~3; }
 
-template <int D, int kSlots>
+// Kept scores (the variant that stores pass 1's scores in LDS): a row of row
+// tile rt holds its 16 (rt + 1) causal-range columns plus 4 floats of pad, so
+// the four row groups of one MFMA result write to different bank groups.
+__host__ __device__ __forceinline__ int score_row(int rt) { return 16 * (rt + 1) + 4; }
+
+// Floats of stored scores a workgroup with S row tiles needs at most: slots
+// hold the tiles P a .. P a + P - 1 and P b .. P b + P - 1 with a + b =
+// ngroups - 1 (or one group alone), so the sum of their score rows is
+// largest for the pair with the most tiles in range.
+__host__ __device__ __forceinline__ int score_floats(int ntiles, int S) {
+  const int P = S > 1 ? S / 2 : 1;
+  const int ng = (ntiles + P - 1) / P;
+  int best = 0;
+  for (int a = 0; a < (S > 1 ? (ng + 1) / 2 : ng); ++a) {
+    const int b = S > 1 ? ng - 1 - a : a;
+    int sum = 0;
+    for (int u = 0; u < S; ++u) {
+      const int rt = u < P ? P * a + u : P * b + u - P;
+      if (rt < ntiles && (u < P || b != a)) sum += 16 * score_row(rt);
+    }
+    best = sum > best ? sum : best;
+  }
+  return best;
+}
+
+template <int D, int kSlots, bool kStore>
 __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict__ qp,
                                                         const float* __restrict__ kp, int Hq, int Hkv,
                                                         int nb, float scale, float ln_tau, int dense,
+                                                        int kmask_off,
                                                         float* __restrict__ row_max,
                                                         int* __restrict__ counts,
                                                         int* __restrict__ indices) {
-  extern __shared__ uint16_t kmask[];  // [16 S local rows][mask_stride]
+  // [stored scores (kStore)][16 S local rows][mask_stride] keep masks
+  extern __shared__ __align__(16) unsigned char dsm[];
   __shared__ float red[4][16 * kSlots];
   __shared__ __align__(16) float mrow[16 * kSlots];  // row maxima of the local rows
 
   const int ntiles = (nb + 15) >> 4;
   const int kst = mask_stride(ntiles);
+  float* const sc = reinterpret_cast<float*>(dsm);
+  uint16_t* const kmask = reinterpret_cast<uint16_t*>(dsm + kmask_off);  // after the scores
   constexpr int P = kSlots > 1 ? kSlots / 2 : 1;  // row tiles per group
   const int ngroups = (ntiles + P - 1) / P;
   // short group (S = 1: the only one, heaviest first)
@@ -90,6 +119,17 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
   // so j <= i  <=>  dl - r <= 16 (rt_u - jt).
   const int dl = c16 - 4 * grp;
   auto slot_tile = [&](int u) { return u < P ? P * a + u : P * b + u - P; };
+  // first stored score of each slot (kStore): slots in order, unused ones
+  // empty; uniform, so these stay in scalar registers
+  int soff[kSlots];
+  {
+    int off = 0;
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      soff[v] = off;
+      if (slot_tile(v) < ntiles && (v < P || two)) off += 16 * score_row(slot_tile(v));
+    }
+  }
 
   // A operands: lane supplies Qbar[16 rt_u + c16][16t + 4grp + c] for slot u
   // in MFMA step (t, c).  Without a long group, its slots repeat the short
@@ -153,9 +193,19 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
 #pragma unroll
     for (int u = U0; u < kSlots; ++u) {
       const int lim = 16 * (slot_tile(u) - jt);
+      float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (dl - r <= lim) mr[u][r] = fmaxf(mr[u][r], acc[u][r] * scale);
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = acc[u][r] * scale;
+        if (dl - r <= lim) mr[u][r] = fmaxf(mr[u][r], sv[r]);
+      }
+      // the scores of key tiles up to the slot's own, for pass 2
+      if (kStore && lim >= 0 && slot_tile(u) < ntiles && (u < P || two)) {
+        const int rl = score_row(slot_tile(u));
+        float* dst = sc + soff[u] + 4 * grp * rl + 16 * jt + c16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[r * rl] = sv[r];
+      }
     }
   };
   auto max_any = [&](const KRows& kr, int jt) {
@@ -232,8 +282,31 @@ __global__ __launch_bounds__(256, 2) void select_kernel(const float* __restrict_
     if (jt <= lo_hi) mask_step(kr, jt, All{});
     else mask_step(kr, jt, Long{});
   };
+  // pass 2 from the stored scores: the same decision on the same bits
+  auto mask_stored = [&](int jt) {
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int rt = slot_tile(u);
+      if (jt > rt || rt >= ntiles || !(u < P || two)) continue;
+      const int lim = 16 * (rt - jt);
+      const int rows_left = nb - 16 * rt;
+      const int rl = score_row(rt);
+      const float* src = sc + soff[u] + 4 * grp * rl + 16 * jt + c16;
+      const floatx4 mu = *reinterpret_cast<const floatx4*>(mrow + 16 * u + 4 * grp);
+      uint64_t bits[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float d = src[r * rl] - mu[r];
+        const bool keep = (dl - r <= lim && 4 * grp + r < rows_left) && (d >= ln_tau || dl - r == lim);
+        bits[r] = __ballot(keep);
+      }
+      put_masks(jt, u, bits);
+    }
+  };
   if (w <= rt_hi) {
-    if (dense) {
+    if (kStore && !dense) {
+      for (int jt = w; jt <= rt_hi; jt += 4) mask_stored(jt);
+    } else if (dense) {
       for (int jt = w; jt <= rt_hi; jt += 4) {
 #pragma unroll
         for (int u = 0; u < kSlots; ++u) {
@@ -327,27 +400,50 @@ hipError_t fpk_launch_select(const FpDims& dm, const float* q_pool, const float*
   constexpr int kMinGroups = 256;
   int S = 4;
   if (groups_of(ntiles, 4) * dm.Hq < kMinGroups) S = groups_of(ntiles, 2) * dm.Hq >= kMinGroups ? 2 : 1;
-  const size_t lds = (size_t)16 * S * mask_stride(ntiles) * sizeof(uint16_t);
-  const int dense = ln_tau == -INFINITY ? 1 : 0;
+  // Pass 1's scores stay in LDS for pass 2 when they fit two workgroups per
+  // CU (the largest S at or below the choice above that fits; at most 2 for
+  // D = 128, whose four-slot variant has no registers left for the stores);
+  // otherwise pass 2 recomputes them.
+  constexpr size_t kStoreLds = 80 * 1024;
+  const bool dense_sel = ln_tau == -INFINITY;
+  bool store = false;
+  for (int s2 = dm.d == 128 ? min(S, 2) : S; s2 >= 1 && !dense_sel; s2 /= 2) {
+    const size_t need = (size_t)score_floats(ntiles, s2) * 4 + (size_t)16 * s2 * mask_stride(ntiles) * 2;
+    if (need <= kStoreLds) {
+      S = s2;
+      store = true;
+      break;
+    }
+  }
+  const size_t kmask_off = store ? (size_t)score_floats(ntiles, S) * 4 : 0;
+  const size_t lds = kmask_off + (size_t)16 * S * mask_stride(ntiles) * sizeof(uint16_t);
+  const int dense = dense_sel ? 1 : 0;
   const dim3 grid((unsigned)(groups_of(ntiles, S) * dm.Hq));
   auto launch = [&](auto kern) -> hipError_t {
-    // 16 S rows x nb bits of masks: up to 128 KiB at 16384 blocks, above the
-    // default 64 KiB dynamic LDS window, so raise the kernel's limit when needed.
+    // 16 S rows x nb bits of masks (and the stored scores): up to 128 KiB at
+    // 16384 blocks, above the default 64 KiB dynamic LDS window, so raise the
+    // kernel's limit when needed.
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, q_pool, k_pool, dm.Hq, dm.Hkv, dm.nb, sm_scale,
-                       ln_tau, dense, row_max, counts, indices);
+                       ln_tau, dense, (int)kmask_off, row_max, counts, indices);
     return hipGetLastError();
   };
   if (dm.d == 128) {
-    if (S == 4) return launch(select_kernel<128, 4>);
-    if (S == 2) return launch(select_kernel<128, 2>);
-    return launch(select_kernel<128, 1>);
+    if (store) return S == 2 ? launch(select_kernel<128, 2, true>) : launch(select_kernel<128, 1, true>);
+    if (S == 4) return launch(select_kernel<128, 4, false>);
+    if (S == 2) return launch(select_kernel<128, 2, false>);
+    return launch(select_kernel<128, 1, false>);
   }
-  if (S == 4) return launch(select_kernel<64, 4>);
-  if (S == 2) return launch(select_kernel<64, 2>);
-  return launch(select_kernel<64, 1>);
+  if (store) {
+    if (S == 4) return launch(select_kernel<64, 4, true>);
+    if (S == 2) return launch(select_kernel<64, 2, true>);
+    return launch(select_kernel<64, 1, true>);
+  }
+  if (S == 4) return launch(select_kernel<64, 4, false>);
+  if (S == 2) return launch(select_kernel<64, 2, false>);
+  return launch(select_kernel<64, 1, false>);
 }
