@@ -1,5 +1,6 @@
 """GPU parity at the benchmarked sizes (32 q / 8 kv heads, d = 128, B = 128,
-L = 32K, 128K, 256K), launched exactly as the benchmark launches them.
+L = 32K, 128K, 256K; and the 32K layer with d or B = 64, which runs the
+64-key-unit attention), launched exactly as the benchmark launches them.
 
 Selection is compared on the whole layer: the oracle pools every block,
 scores every causal block pair one head at a time, thresholds and takes its
@@ -24,10 +25,16 @@ from tests.parity_util import POOL_RTOL, TOL, require_gpu, say
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    ("c3", 0.05), ("c3", 0.1), ("c3", 0.2),
-    ("c4", 0.1), ("c4_fp8", 0.1), ("c4_dense", 0.0),
-    ("c5", 0.1),
+    ("c3", 0.05, {}), ("c3", 0.1, {}), ("c3", 0.2, {}),
+    ("c3", 0.05, {"head_dim": 64}), ("c3", 0.05, {"head_dim": 64, "block_size": 64}),
+    ("c3", 0.05, {"block_size": 64}),
+    ("c4", 0.1, {}), ("c4_fp8", 0.1, {}), ("c4_dense", 0.0, {}),
+    ("c5", 0.1, {}),
 ]
+
+
+def _case_id(n, t, over):
+    return f"{n}_tau{t}" + "".join(f"_{'d' if k == 'head_dim' else 'B'}{v}" for k, v in over.items())
 
 
 def _host(t, scale, g=None):
@@ -94,13 +101,13 @@ def sample_rows(counts, nb, seed=0, per_head=8):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name,tau", CASES, ids=[f"{n}_tau{t}" for n, t in CASES])
-def test_full_size_parity(name, tau):
+@pytest.mark.parametrize("name,tau,over", CASES, ids=[_case_id(*c) for c in CASES])
+def test_full_size_parity(name, tau, over):
     dev = require_gpu()
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name].with_(**over)
     L, B, Hq, Hkv, d = cfg.seq_len, cfg.block_size, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     G, nb = Hq // Hkv, cfg.num_blocks
-    say(f"[full {name} tau={tau}] L={L} {cfg.dtype}")
+    say(f"[full {name} tau={tau}] L={L} d={d} B={B} {cfg.dtype}")
     lay = make_layer(cfg, device=dev, keep_fp32=False)
     pf = _lib.Prefill(lay.q, lay.k, lay.v, block_size=B, threshold=tau,
                       q_scale=lay.q_scale, k_scale=lay.k_scale, v_scale=lay.v_scale)
