@@ -107,17 +107,23 @@ def test_dense_lists_past_one_window(d, B, L):
     check_out(res["out"], dense, "bf16")
 
 
-@pytest.mark.parametrize("L", [1, 77, 128, 129, 256])
-def test_degenerate_lengths(L):
+DEGENERATE = [(L, 128, 128) for L in (1, 77, 128, 129, 256)] + [
+    # the 64-key-unit kernel: a block whose second unit lies wholly past L,
+    # one-token and one-block layers
+    (L, d, B) for (d, B) in ((64, 128), (64, 64), (128, 64)) for L in (1, 63, 65, 129)]
+
+
+@pytest.mark.parametrize("L,d,B", DEGENERATE, ids=[f"L{L}_d{d}_B{B}" for L, d, B in DEGENERATE])
+def test_degenerate_lengths(L, d, B):
     dev = require_gpu()
-    cfg = CONFIGS["c2"].with_(seq_len=L, num_q_heads=4, num_kv_heads=2)
-    say(f"[length {L}]")
+    cfg = CONFIGS["c2"].with_(seq_len=L, num_q_heads=4, num_kv_heads=2, head_dim=d, block_size=B)
+    say(f"[length {L} d={d} B={B}]")
     layer = make_layer(cfg)
     ref = oracle_full(layer, 0.1)
     _, res = run_gpu(layer, 0.1, dev)
     bad, _ = selection_mismatch(res["lists"], ref["keep"], ref["amb"])
     assert bad == 0
-    want = O.sparse_attention(ref["q"], ref["k"], ref["v"], res["lists"], 128, sm_scale(layer))
+    want = O.sparse_attention(ref["q"], ref["k"], ref["v"], res["lists"], B, sm_scale(layer))
     check_out(res["out"], want, "bf16")
     if L == 1:
         # one token attends to itself only
