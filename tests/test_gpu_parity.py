@@ -31,6 +31,14 @@ CASES = {
     "bf16_d128_b64": ("c2", {"seq_len": 1100, "num_q_heads": 4, "num_kv_heads": 1,
                              "block_size": 64}, 0.2),
     "fp8_ragged": ("c4_fp8", {"seq_len": 1000, "num_q_heads": 8, "num_kv_heads": 2}, 0.1),
+    # e4m3 with d = B = 64 and with B = 64 only: the vector-ALU attention
+    "fp8_d64_b64": ("c4_fp8", {"seq_len": 1100, "num_q_heads": 4, "num_kv_heads": 2,
+                               "head_dim": 64, "block_size": 64}, 0.1),
+    "fp8_d128_b64": ("c4_fp8", {"seq_len": 900, "num_q_heads": 4, "num_kv_heads": 1,
+                                "block_size": 64}, 0.1),
+    # bf16 with d = 64, B = 128 (the 64-key-unit kernel, two units per block)
+    "bf16_d64_b128": ("c2", {"seq_len": 1300, "num_q_heads": 6, "num_kv_heads": 2,
+                             "head_dim": 64}, 0.1),
     "f32_d128_b128": ("c2", {"seq_len": 700, "num_q_heads": 2, "num_kv_heads": 1,
                              "dtype": "f32"}, 0.1),
     # three q heads per kv head and 4 kv heads: the attention's plain work order
