@@ -83,6 +83,25 @@ def test_workspace_layout_sizes_and_alignment():
     assert lay32.total == lay32.v_t  # no V^T for fp32 inputs
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("d,B", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_vt_section_follows_the_attention_dispatch(dtype, d, B):
+    # The V^T section exists exactly when the attention runs on the matrix
+    # cores (its kernels read V^T): bf16 or e4m3 with d = B = 128, bf16 with
+    # d and B in {64, 128}.  The host computes the layout, so the dispatch
+    # rule is checked here without a GPU, against the same rule bench.py
+    # uses to name the kernel it measures.
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    code = {"f32": fp.FP_F32, "bf16": fp.FP_BF16, "fp8": fp.FP_FP8_E4M3}[dtype]
+    lay = fp.fp_workspace_layout(prob(dtype=code, head_dim=d, block_size=B))
+    nb = (1000 + B - 1) // B
+    matrix = bench.attention_kernel(dtype, d, B) != "generic"
+    assert lay.total - lay.v_t == (2 * d * nb * B * 2 if matrix else 0)
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("threshold", float("nan"), fp.FP_ERR_INVALID),
     ("threshold", -0.01, fp.FP_ERR_INVALID),
